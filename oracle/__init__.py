@@ -1,0 +1,19 @@
+"""CPU oracle for the Moshi RQ-Transformer frame step -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The HIP library never calls it and shares no code with it.
+"""
+from .moshi_oracle import (  # noqa: F401
+    ALPHA,
+    Oracle,
+    Session,
+    causal_attention,
+    cross_entropy_loss,
+    delay_codes,
+    joint_sequence,
+    rms_norm,
+    rope,
+    silu,
+    top2_margin,
+    undelay_codes,
+)
