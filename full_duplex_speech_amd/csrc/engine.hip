@@ -1,0 +1,980 @@
+// Host engine and C ABI (include/moshi.h): workspace plan, weight repack, KV
+// page pool, frame-step sequencing with hipGraph replay, teacher-forced scoring.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <functional>
+#include <map>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/moshi.h"
+#include "moshi_internal.h"
+
+using namespace moshi;
+
+namespace {
+
+struct Error {
+  int code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  throw Error{code, buf};
+}
+
+#define HIPCHECK(expr)                                                                   \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess) fail(MOSHI_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+std::string g_create_error;
+
+struct LayerW {
+  size_t wqkv, wo, wgu, wdown, attn_norm, ffn_norm;
+};
+struct DepthW {
+  size_t in_proj, emb, out_norm, head;
+  std::vector<LayerW> layers;
+};
+struct Dest {
+  size_t off;      // byte offset of the destination region
+  long long rows;  // source rows
+  int cols;        // source columns
+  long long mult, add;
+  bool f32;        // stored as float32 regardless of dtype
+  bool loaded;
+};
+
+struct Plan {
+  bool bf = false;
+  int esz = 4;
+  size_t total = 0;
+  size_t take(size_t bytes) {
+    size_t o = (total + 255) & ~(size_t)255;
+    total = o + bytes;
+    return o;
+  }
+  // weights
+  size_t emb_t = 0;
+  long long emb_row0[kStreams];
+  int emb_rows[kStreams];
+  std::vector<LayerW> lt;
+  size_t out_norm = 0, text_head = 0;
+  std::vector<DepthW> dj;
+  // tables
+  size_t meta_row0 = 0, meta_rows = 0, rope_t = 0, rope_d = 0;
+  // KV
+  size_t kv_pages = 0, page_table = 0, depth_kv = 0;
+  long long page_elems = 0, depth_kv_elems = 0;
+  int max_pages_conv = 0, n_pages = 0, max_splits = 0;
+  // state (int32)
+  size_t st_pos = 0, st_prev = 0, st_in = 0, st_out_tok = 0, st_cur_tok = 0, st_err = 0, st_cnt_t = 0,
+         st_cnt_d = 0, st_end = 0;
+  size_t st_user = 0, st_force = 0, st_has_force = 0;
+  // activations (float32)
+  size_t h = 0, q = 0, attn = 0, inter = 0, part_t = 0, text_logits = 0;
+  size_t hd = 0, dq = 0, dattn = 0, dinter = 0, part_d = 0, audio_logits = 0;
+  // teacher-forced
+  size_t tf_tokens = 0, tf_ce = 0, tf_res = 0;
+  size_t staging = 0, staging_bytes = 0;
+};
+
+int validate(const moshi_config& c, std::string& msg) {
+  auto bad = [&](const char* m) {
+    msg = m;
+    return MOSHI_EINVAL;
+  };
+  if (c.d_t <= 0 || c.n_layers_t <= 0 || c.n_heads_t <= 0 || c.ffn_t <= 0 || c.ctx_max <= 0)
+    return bad("temporal sizes must be positive");
+  if (c.d_d <= 0 || c.n_layers_d <= 0 || c.n_heads_d <= 0 || c.ffn_d <= 0) return bad("depth sizes must be positive");
+  if (c.d_t % c.n_heads_t || c.d_d % c.n_heads_d) return bad("model width must be a multiple of the head count");
+  int hdt = c.d_t / c.n_heads_t, hdd = c.d_d / c.n_heads_d;
+  if ((hdt != 32 && hdt != 64 && hdt != 128) || (hdd != 32 && hdd != 64 && hdd != 128))
+    return bad("head dims must be 32, 64 or 128");
+  if (c.d_t % 16 || c.d_d % 16) return bad("model widths must be multiples of 16");
+  if (c.ffn_t % 8 || c.ffn_d % 8) return bad("SwiGLU widths must be multiples of 8");
+  if (c.n_q != 8) return bad("n_q must be 8 (K = 17 sub-streams)");
+  if (c.vocab_text < 2 || c.codebook < 2) return bad("vocabularies must have at least 2 entries");
+  if (c.delay < 0) return bad("delay must be >= 0");
+  if (!(c.rope_base > 0.f) || !(c.norm_eps > 0.f)) return bad("rope_base and norm_eps must be positive");
+  if (c.dtype != MOSHI_F32 && c.dtype != MOSHI_BF16) return bad("dtype must be MOSHI_F32 or MOSHI_BF16");
+  if (c.max_batch < 1 || c.max_batch > kMaxBatch) return bad("max_batch must be in 1..8");
+  if (c.page_frames != 8 && c.page_frames != 16 && c.page_frames != 32 && c.page_frames != 64)
+    return bad("page_frames must be 8, 16, 32 or 64");
+  if (c.n_pages < 0 || c.max_tf_tokens < 0) return bad("n_pages and max_tf_tokens must be >= 0");
+  return MOSHI_OK;
+}
+
+Plan make_plan(const moshi_config& c) {
+  Plan p;
+  p.bf = c.dtype == MOSHI_BF16;
+  p.esz = p.bf ? 2 : 4;
+  const size_t e = p.esz;
+  const long long d = c.d_t, F = c.ffn_t, dd = c.d_d, Fd = c.ffn_d;
+  long long rows = 0;
+  for (int k = 0; k < kStreams; ++k) {
+    p.emb_row0[k] = rows;
+    p.emb_rows[k] = (k == 0 ? c.vocab_text : c.codebook) + 1;
+    rows += p.emb_rows[k];
+  }
+  p.emb_t = p.take(rows * d * e);
+  for (int l = 0; l < c.n_layers_t; ++l) {
+    LayerW w;
+    w.wqkv = p.take(3 * d * d * e);
+    w.wo = p.take(d * d * e);
+    w.wgu = p.take(2 * F * d * e);
+    w.wdown = p.take(d * F * e);
+    w.attn_norm = p.take(d * 4);
+    w.ffn_norm = p.take(d * 4);
+    p.lt.push_back(w);
+  }
+  p.out_norm = p.take(d * 4);
+  p.text_head = p.take((long long)c.vocab_text * d * e);
+  for (int j = 0; j < c.n_q; ++j) {
+    DepthW w;
+    w.in_proj = p.take(dd * d * e);
+    w.emb = p.take((long long)((j == 0 ? c.vocab_text : c.codebook) + 1) * dd * e);
+    for (int l = 0; l < c.n_layers_d; ++l) {
+      LayerW x;
+      x.wqkv = p.take(3 * dd * dd * e);
+      x.wo = p.take(dd * dd * e);
+      x.wgu = p.take(2 * Fd * dd * e);
+      x.wdown = p.take(dd * Fd * e);
+      x.attn_norm = p.take(dd * 4);
+      x.ffn_norm = p.take(dd * 4);
+      w.layers.push_back(x);
+    }
+    w.out_norm = p.take(dd * 4);
+    w.head = p.take((long long)c.codebook * dd * e);
+    p.dj.push_back(w);
+  }
+  p.meta_row0 = p.take(kStreams * 8);
+  p.meta_rows = p.take(kStreams * 4);
+  const int hdt = c.d_t / c.n_heads_t, hdd = c.d_d / c.n_heads_d;
+  p.rope_t = p.take((size_t)c.ctx_max * hdt * 4);
+  p.rope_d = p.take((size_t)c.n_q * hdd * 4);
+  // paged temporal KV (bf16 for bf16 models), flat depth KV (float32)
+  p.max_pages_conv = (c.ctx_max + c.page_frames - 1) / c.page_frames;
+  p.n_pages = c.n_pages ? c.n_pages : c.max_batch * p.max_pages_conv;
+  p.page_elems = (long long)c.n_layers_t * 2 * c.d_t * c.page_frames;
+  p.kv_pages = p.take((size_t)p.n_pages * p.page_elems * e);
+  p.page_table = p.take((size_t)c.max_batch * p.max_pages_conv * 4);
+  p.depth_kv_elems = (long long)c.n_layers_d * 2 * c.d_d * c.n_q;
+  p.depth_kv = p.take((size_t)c.max_batch * p.depth_kv_elems * 4);
+  p.max_splits = p.max_pages_conv;
+  // state
+  const int mb = c.max_batch;
+  p.st_pos = p.take(mb * 4);
+  p.st_prev = p.take(mb * kStreams * 4);
+  p.st_in = p.take((mb * 8 + mb * kSlots + 1) * 4);
+  p.st_user = p.st_in;
+  p.st_force = p.st_in + mb * 8 * 4;
+  p.st_has_force = p.st_force + mb * kSlots * 4;
+  p.st_out_tok = p.take(mb * kSlots * 4);
+  p.st_cur_tok = p.take(mb * kSlots * 4);
+  p.st_err = p.take(4);
+  p.st_cnt_t = p.take(mb * c.n_heads_t * 4);
+  p.st_cnt_d = p.take(mb * c.n_heads_d * 4);
+  p.st_end = p.total;
+  // activations
+  p.h = p.take(mb * d * 4);
+  p.q = p.take(mb * d * 4);
+  p.attn = p.take(mb * d * 4);
+  p.inter = p.take(mb * F * 4);
+  p.part_t = p.take((size_t)mb * c.n_heads_t * p.max_splits * (hdt + 2) * 4);
+  p.text_logits = p.take((size_t)mb * c.vocab_text * 4);
+  p.hd = p.take(mb * dd * 4);
+  p.dq = p.take(mb * dd * 4);
+  p.dattn = p.take(mb * dd * 4);
+  p.dinter = p.take(mb * Fd * 4);
+  p.part_d = p.take((size_t)mb * c.n_heads_d * (hdd + 2) * 4);
+  p.audio_logits = p.take((size_t)mb * c.n_q * c.codebook * 4);
+  // teacher-forced
+  const long long tf = c.max_tf_tokens ? c.max_tf_tokens : (long long)c.ctx_max * mb;
+  p.tf_tokens = p.take((size_t)tf * kStreams * 4);
+  p.tf_ce = p.take((size_t)tf * kSlots * 8);
+  p.tf_res = p.take(32 * 8);
+  p.staging_bytes = 64ull << 20;
+  p.staging = p.take(p.staging_bytes);
+  p.total = (p.total + 255) & ~(size_t)255;
+  return p;
+}
+
+}  // namespace
+
+struct moshi_ctx {
+  moshi_config cfg;
+  Plan plan;
+  char* ws = nullptr;
+  hipStream_t stream = nullptr;      // owned
+  hipStream_t caller = nullptr;      // optional caller stream
+  hipEvent_t ev_in = nullptr, ev_out = nullptr;
+  int device = 0;
+  std::map<std::string, Dest> dests;
+  size_t n_loaded = 0;
+  bool ready = false;
+  bool use_graph = true;
+  std::map<std::pair<int, int>, hipGraphExec_t> graphs;
+  // host mirrors
+  std::vector<int> pos_h;
+  std::vector<std::vector<int>> pages;
+  std::vector<int> free_pages;
+  int* pinned = nullptr;  // staging: inputs block, outputs, page table mirror, constants
+  size_t pinned_ints = 0;
+  int* pin_in = nullptr;
+  int* pin_out = nullptr;
+  int* pin_pt = nullptr;
+  int* pin_one = nullptr;
+  int* pin_zero = nullptr;
+  double* pin_res = nullptr;
+  std::string err;
+
+  template <typename T>
+  T* at(size_t off) const {
+    return (T*)(ws + off);
+  }
+};
+
+namespace {
+
+void add_dest(moshi_ctx* c, const std::string& name, size_t off, long long rows, int cols, long long mult = 1,
+              long long add = 0, bool f32 = false) {
+  c->dests[name] = Dest{off, rows, cols, mult, add, f32, false};
+}
+
+void build_dests(moshi_ctx* c) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const size_t e = p.esz;
+  const long long d = g.d_t, dd = g.d_d;
+  for (int k = 0; k < kStreams; ++k)
+    add_dest(c, "temporal.emb." + std::to_string(k), p.emb_t + p.emb_row0[k] * d * e, p.emb_rows[k], (int)d);
+  auto layer = [&](const std::string& pre, const LayerW& w, long long D, long long F) {
+    add_dest(c, pre + "attn_norm", w.attn_norm, 1, (int)D, 1, 0, true);
+    add_dest(c, pre + "ffn_norm", w.ffn_norm, 1, (int)D, 1, 0, true);
+    add_dest(c, pre + "wq", w.wqkv, D, (int)D);
+    add_dest(c, pre + "wk", w.wqkv + D * D * e, D, (int)D);
+    add_dest(c, pre + "wv", w.wqkv + 2 * D * D * e, D, (int)D);
+    add_dest(c, pre + "wo", w.wo, D, (int)D);
+    add_dest(c, pre + "w_gate", w.wgu, F, (int)D, 2, 0);  // gate rows at 2i
+    add_dest(c, pre + "w_up", w.wgu, F, (int)D, 2, 1);    // up rows at 2i+1
+    add_dest(c, pre + "w_down", w.wdown, D, (int)F);
+  };
+  for (int l = 0; l < g.n_layers_t; ++l) layer("temporal.layers." + std::to_string(l) + ".", p.lt[l], d, g.ffn_t);
+  add_dest(c, "temporal.out_norm", p.out_norm, 1, (int)d, 1, 0, true);
+  add_dest(c, "temporal.text_head", p.text_head, g.vocab_text, (int)d);
+  for (int j = 0; j < g.n_q; ++j) {
+    const std::string pre = "depth." + std::to_string(j) + ".";
+    const DepthW& w = p.dj[j];
+    add_dest(c, pre + "in_proj", w.in_proj, dd, (int)d);
+    add_dest(c, pre + "emb", w.emb, (j == 0 ? g.vocab_text : g.codebook) + 1, (int)dd);
+    for (int l = 0; l < g.n_layers_d; ++l) layer(pre + "layers." + std::to_string(l) + ".", w.layers[l], dd, g.ffn_d);
+    add_dest(c, pre + "out_norm", w.out_norm, 1, (int)dd, 1, 0, true);
+    add_dest(c, pre + "head", w.head, g.codebook, (int)dd);
+  }
+}
+
+void order_in(moshi_ctx* c) {
+  if (c->caller) {
+    HIPCHECK(hipEventRecord(c->ev_in, c->caller));
+    HIPCHECK(hipStreamWaitEvent(c->stream, c->ev_in, 0));
+  }
+}
+void order_out(moshi_ctx* c) {
+  if (c->caller) {
+    HIPCHECK(hipEventRecord(c->ev_out, c->stream));
+    HIPCHECK(hipStreamWaitEvent(c->caller, c->ev_out, 0));
+  }
+}
+
+KvView temporal_kv(moshi_ctx* c) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  KvView v;
+  v.base = c->ws + p.kv_pages;
+  v.page_table = c->at<int>(p.page_table);
+  v.pt_stride = p.max_pages_conv;
+  v.page_stride = p.page_elems;
+  v.pf = g.page_frames;
+  v.n_heads = g.n_heads_t;
+  v.hd = g.d_t / g.n_heads_t;
+  return v;
+}
+
+KvView depth_kv(moshi_ctx* c) {
+  const moshi_config& g = c->cfg;
+  KvView v;
+  v.base = c->ws + c->plan.depth_kv;
+  v.page_table = nullptr;
+  v.pt_stride = 0;
+  v.page_stride = c->plan.depth_kv_elems;
+  v.pf = g.n_q;
+  v.n_heads = g.n_heads_d;
+  v.hd = g.d_d / g.n_heads_d;
+  return v;
+}
+
+// Enqueue one frame for conversations 0..B-1 (no host interaction).
+void enqueue_step(moshi_ctx* c, int B, bool depth) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  hipStream_t s = c->stream;
+  const bool bf = p.bf;
+  const int d = g.d_t, F = g.ffn_t, dd = g.d_d, Fd = g.ffn_d;
+  const int hdt = d / g.n_heads_t, hdd = dd / g.n_heads_d;
+  int* pos = c->at<int>(p.st_pos);
+  int* cur = c->at<int>(p.st_cur_tok);
+
+  EmbedArgs ea{};
+  ea.table = c->ws + p.emb_t;
+  ea.row0 = c->at<long long>(p.meta_row0);
+  ea.rows = c->at<int>(p.meta_rows);
+  ea.frames = c->at<int>(p.st_prev);
+  ea.h = c->at<float>(p.h);
+  ea.d = d;
+  ea.err = c->at<int>(p.st_err);
+  launch_embed(ea, B, bf, s);
+
+  const KvView tkv = temporal_kv(c);
+  for (int l = 0; l < g.n_layers_t; ++l) {
+    const LayerW& w = p.lt[l];
+    GemvArgs a{};
+    a.eps = g.norm_eps;
+    // RMSNorm -> Wq|Wk|Wv -> RoPE -> q, KV append
+    a.W = c->ws + w.wqkv;
+    a.N = 3 * d;
+    a.K = d;
+    a.x = c->at<float>(p.h);
+    a.ldx = d;
+    a.gain = c->at<float>(w.attn_norm);
+    a.y = c->at<float>(p.q);
+    a.ldy = d;
+    a.pos = pos;
+    a.rope = c->at<float>(p.rope_t);
+    a.hd = hdt;
+    a.d = d;
+    a.kv = tkv;
+    a.kv_bf16 = bf;
+    a.layer = l;
+    launch_gemv(a, B, EPI_QKV, bf, s);
+    // attention over positions 0..pos
+    AttnArgs at{};
+    at.q = c->at<float>(p.q);
+    at.ldq = d;
+    at.kv = tkv;
+    at.layer = l;
+    at.pos = pos;
+    at.split = g.page_frames;
+    at.part = c->at<float>(p.part_t);
+    at.max_splits = p.max_splits;
+    at.counters = c->at<int>(p.st_cnt_t);
+    at.out = c->at<float>(p.attn);
+    at.ldo = d;
+    at.scale = 1.0f / sqrtf((float)hdt);
+    launch_attn_decode(at, B, g.n_heads_t, hdt, bf, s);
+    // h += Wo attn
+    GemvArgs o{};
+    o.W = c->ws + w.wo;
+    o.N = d;
+    o.K = d;
+    o.x = c->at<float>(p.attn);
+    o.ldx = d;
+    o.y = c->at<float>(p.h);
+    o.ldy = d;
+    launch_gemv(o, B, EPI_RESID, bf, s);
+    // SwiGLU: inter = SiLU(Wg n) * (Wu n), n = RMSNorm(h)
+    GemvArgs f{};
+    f.eps = g.norm_eps;
+    f.W = c->ws + w.wgu;
+    f.N = 2 * F;
+    f.K = d;
+    f.x = c->at<float>(p.h);
+    f.ldx = d;
+    f.gain = c->at<float>(w.ffn_norm);
+    f.y = c->at<float>(p.inter);
+    f.ldy = F;
+    launch_gemv(f, B, EPI_SWIGLU, bf, s);
+    // h += Wdown inter
+    GemvArgs dn{};
+    dn.W = c->ws + w.wdown;
+    dn.N = d;
+    dn.K = F;
+    dn.x = c->at<float>(p.inter);
+    dn.ldx = F;
+    dn.y = c->at<float>(p.h);
+    dn.ldy = d;
+    launch_gemv(dn, B, EPI_RESID, bf, s);
+  }
+  // text head on z = RMSNorm(h), greedy text token
+  {
+    GemvArgs a{};
+    a.eps = g.norm_eps;
+    a.W = c->ws + p.text_head;
+    a.N = g.vocab_text;
+    a.K = d;
+    a.x = c->at<float>(p.h);
+    a.ldx = d;
+    a.gain = c->at<float>(p.out_norm);
+    a.y = c->at<float>(p.text_logits);
+    a.ldy = g.vocab_text;
+    launch_gemv(a, B, EPI_STORE, bf, s);
+    ArgmaxArgs m{};
+    m.logits = c->at<float>(p.text_logits);
+    m.n = g.vocab_text;
+    m.ld = g.vocab_text;
+    m.slot = 0;
+    m.pad_after = 0;
+    m.pos = pos;
+    m.out_tok = c->at<int>(p.st_out_tok);
+    m.cur_tok = cur;
+    m.force = c->at<int>(p.st_force);
+    m.has_force = c->at<int>(p.st_has_force);
+    launch_argmax(m, B, s);
+  }
+  if (depth) {
+    const KvView dkv = depth_kv(c);
+    for (int j = 0; j < g.n_q; ++j) {
+      const DepthW& w = p.dj[j];
+      // u_j = W_in^j z + E_D^j[token of slot j]
+      GemvArgs a{};
+      a.eps = g.norm_eps;
+      a.W = c->ws + w.in_proj;
+      a.N = dd;
+      a.K = d;
+      a.x = c->at<float>(p.h);
+      a.ldx = d;
+      a.gain = c->at<float>(p.out_norm);
+      a.y = c->at<float>(p.hd);
+      a.ldy = dd;
+      a.emb = c->ws + w.emb;
+      a.tok = cur;
+      a.tok_stride = kSlots;
+      a.tok_col = j;
+      a.tok_rows = (j == 0 ? g.vocab_text : g.codebook) + 1;
+      launch_gemv(a, B, EPI_EMB, bf, s);
+      for (int l = 0; l < g.n_layers_d; ++l) {
+        const LayerW& lw = w.layers[l];
+        GemvArgs q{};
+        q.eps = g.norm_eps;
+        q.W = c->ws + lw.wqkv;
+        q.N = 3 * dd;
+        q.K = dd;
+        q.x = c->at<float>(p.hd);
+        q.ldx = dd;
+        q.gain = c->at<float>(lw.attn_norm);
+        q.y = c->at<float>(p.dq);
+        q.ldy = dd;
+        q.pos = nullptr;
+        q.pos_const = j;
+        q.rope = c->at<float>(p.rope_d);
+        q.hd = hdd;
+        q.d = dd;
+        q.kv = dkv;
+        q.kv_bf16 = 0;
+        q.layer = l;
+        launch_gemv(q, B, EPI_QKV, bf, s);
+        AttnArgs at{};
+        at.q = c->at<float>(p.dq);
+        at.ldq = dd;
+        at.kv = dkv;
+        at.layer = l;
+        at.pos = nullptr;
+        at.pos_const = j;
+        at.split = g.n_q;
+        at.part = c->at<float>(p.part_d);
+        at.max_splits = 1;
+        at.counters = c->at<int>(p.st_cnt_d);
+        at.out = c->at<float>(p.dattn);
+        at.ldo = dd;
+        at.scale = 1.0f / sqrtf((float)hdd);
+        launch_attn_decode(at, B, g.n_heads_d, hdd, false, s);
+        GemvArgs o{};
+        o.W = c->ws + lw.wo;
+        o.N = dd;
+        o.K = dd;
+        o.x = c->at<float>(p.dattn);
+        o.ldx = dd;
+        o.y = c->at<float>(p.hd);
+        o.ldy = dd;
+        launch_gemv(o, B, EPI_RESID, bf, s);
+        GemvArgs f{};
+        f.eps = g.norm_eps;
+        f.W = c->ws + lw.wgu;
+        f.N = 2 * Fd;
+        f.K = dd;
+        f.x = c->at<float>(p.hd);
+        f.ldx = dd;
+        f.gain = c->at<float>(lw.ffn_norm);
+        f.y = c->at<float>(p.dinter);
+        f.ldy = Fd;
+        launch_gemv(f, B, EPI_SWIGLU, bf, s);
+        GemvArgs dn{};
+        dn.W = c->ws + lw.wdown;
+        dn.N = dd;
+        dn.K = Fd;
+        dn.x = c->at<float>(p.dinter);
+        dn.ldx = Fd;
+        dn.y = c->at<float>(p.hd);
+        dn.ldy = dd;
+        launch_gemv(dn, B, EPI_RESID, bf, s);
+      }
+      GemvArgs hh{};
+      hh.eps = g.norm_eps;
+      hh.W = c->ws + w.head;
+      hh.N = g.codebook;
+      hh.K = dd;
+      hh.x = c->at<float>(p.hd);
+      hh.ldx = dd;
+      hh.gain = c->at<float>(w.out_norm);
+      hh.y = c->at<float>(p.audio_logits) + (long long)j * g.codebook;
+      hh.ldy = g.n_q * g.codebook;
+      launch_gemv(hh, B, EPI_STORE, bf, s);
+      ArgmaxArgs m{};
+      m.logits = c->at<float>(p.audio_logits) + (long long)j * g.codebook;
+      m.n = g.codebook;
+      m.ld = g.n_q * g.codebook;
+      m.slot = j + 1;
+      m.pad_after = j >= 1;
+      m.pad_id = g.codebook;
+      m.delay = g.delay;
+      m.pos = pos;
+      m.out_tok = c->at<int>(p.st_out_tok);
+      m.cur_tok = cur;
+      m.force = c->at<int>(p.st_force);
+      m.has_force = c->at<int>(p.st_has_force);
+      launch_argmax(m, B, s);
+    }
+  }
+  AdvanceArgs av{};
+  av.cur_tok = cur;
+  av.force = c->at<int>(p.st_force);
+  av.has_force = c->at<int>(p.st_has_force);
+  av.user = c->at<int>(p.st_user);
+  av.prev = c->at<int>(p.st_prev);
+  av.pos = pos;
+  av.err = c->at<int>(p.st_err);
+  av.pad_text = g.vocab_text;
+  av.pad_audio = g.codebook;
+  launch_advance(av, B, s);
+  HIPCHECK(hipGetLastError());
+}
+
+void run_step(moshi_ctx* c, int B, bool depth) {
+  if (!c->use_graph) {
+    enqueue_step(c, B, depth);
+    return;
+  }
+  auto key = std::make_pair(B, depth ? 1 : 0);
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    hipGraph_t graph;
+    HIPCHECK(hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
+    try {
+      enqueue_step(c, B, depth);
+    } catch (...) {
+      (void)hipStreamEndCapture(c->stream, &graph);
+      throw;
+    }
+    HIPCHECK(hipStreamEndCapture(c->stream, &graph));
+    hipGraphExec_t exec;
+    HIPCHECK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+    HIPCHECK(hipGraphDestroy(graph));
+    it = c->graphs.emplace(key, exec).first;
+  }
+  HIPCHECK(hipGraphLaunch(it->second, c->stream));
+}
+
+// make sure conversation b has KV pages for positions < upto
+void ensure_pages(moshi_ctx* c, int b, int upto) {
+  const int pf = c->cfg.page_frames;
+  const int need = (upto + pf - 1) / pf;
+  auto& pg = c->pages[b];
+  while ((int)pg.size() < need) {
+    if (c->free_pages.empty()) fail(MOSHI_ENOMEM, "KV page pool exhausted (%d pages)", c->plan.n_pages);
+    const int phys = c->free_pages.back();
+    c->free_pages.pop_back();
+    const int idx = b * c->plan.max_pages_conv + (int)pg.size();
+    pg.push_back(phys);
+    c->pin_pt[idx] = phys;
+    HIPCHECK(hipMemcpyAsync(c->at<int>(c->plan.page_table) + idx, c->pin_pt + idx, 4, hipMemcpyHostToDevice,
+                            c->stream));
+  }
+}
+
+void reset_conv(moshi_ctx* c, int b) {
+  HIPCHECK(hipStreamSynchronize(c->stream));
+  for (int ph : c->pages[b]) c->free_pages.push_back(ph);
+  c->pages[b].clear();
+  c->pos_h[b] = 0;
+  int frame[kStreams];
+  frame[0] = c->cfg.vocab_text;
+  for (int k = 1; k < kStreams; ++k) frame[k] = c->cfg.codebook;
+  int zero = 0;
+  HIPCHECK(hipMemcpy(c->at<int>(c->plan.st_prev) + b * kStreams, frame, sizeof frame, hipMemcpyHostToDevice));
+  HIPCHECK(hipMemcpy(c->at<int>(c->plan.st_pos) + b, &zero, 4, hipMemcpyHostToDevice));
+}
+
+void check_ids(const int32_t* v, long long n, int stride, int first_slot, const moshi_config& g) {
+  for (long long i = 0; i < n; ++i) {
+    const int slot = first_slot + (int)(i % stride);
+    const int hi = slot == 0 ? g.vocab_text : g.codebook;
+    if (v[i] < 0 || v[i] > hi) fail(MOSHI_EINVAL, "token id %d out of range [0, %d] in slot %d", v[i], hi, slot);
+  }
+}
+
+int guard_impl(moshi_ctx* c, const std::function<void()>& fn) {
+  try {
+    fn();
+    return MOSHI_OK;
+  } catch (const Error& e) {
+    if (c) c->err = e.msg;
+    return e.code;
+  } catch (const std::exception& e) {
+    if (c) c->err = e.what();
+    return MOSHI_EINVAL;
+  }
+}
+}  // namespace
+
+extern "C" {
+
+size_t moshi_workspace_bytes(const moshi_config* cfg) {
+  if (!cfg) return 0;
+  std::string msg;
+  if (validate(*cfg, msg) != MOSHI_OK) return 0;
+  return make_plan(*cfg).total;
+}
+
+int moshi_check_config(const moshi_config* cfg, char* msg, size_t msg_len) {
+  std::string m;
+  int rc = cfg ? validate(*cfg, m) : (m = "null config", MOSHI_EINVAL);
+  if (msg && msg_len) {
+    snprintf(msg, msg_len, "%s", m.c_str());
+  }
+  return rc;
+}
+
+int moshi_create(const moshi_config* cfg, void* hip_stream, void* workspace, size_t ws_bytes, moshi_ctx** out) {
+  if (!out) {
+    g_create_error = "out is null";
+    return MOSHI_EINVAL;
+  }
+  *out = nullptr;
+  if (!cfg) {
+    g_create_error = "null config";
+    return MOSHI_EINVAL;
+  }
+  std::string msg;
+  if (validate(*cfg, msg) != MOSHI_OK) {
+    g_create_error = msg;
+    return MOSHI_EINVAL;
+  }
+  Plan plan = make_plan(*cfg);
+  if (!workspace) {
+    g_create_error = "workspace is null";
+    return MOSHI_EINVAL;
+  }
+  if (ws_bytes < plan.total) {
+    char buf[160];
+    snprintf(buf, sizeof buf, "workspace of %zu bytes, %zu needed", ws_bytes, plan.total);
+    g_create_error = buf;
+    return MOSHI_ENOMEM;
+  }
+  moshi_ctx* c = new moshi_ctx();
+  c->cfg = *cfg;
+  c->plan = plan;
+  c->ws = (char*)workspace;
+  c->caller = (hipStream_t)hip_stream;
+  const char* ng = getenv("MOSHI_NO_GRAPH");
+  c->use_graph = !(ng && ng[0] == '1');
+  int rc = guard_impl(c, [&] {
+    HIPCHECK(hipGetDevice(&c->device));
+    HIPCHECK(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
+    HIPCHECK(hipEventCreateWithFlags(&c->ev_in, hipEventDisableTiming));
+    HIPCHECK(hipEventCreateWithFlags(&c->ev_out, hipEventDisableTiming));
+    const Plan& p = c->plan;
+    const int mb = cfg->max_batch;
+    c->pinned_ints = mb * 8 + mb * kSlots + 1 + mb * kSlots + (size_t)mb * p.max_pages_conv + 2 + 64;
+    HIPCHECK(hipHostMalloc((void**)&c->pinned, c->pinned_ints * 4 + 32 * 8, hipHostMallocDefault));
+    c->pin_in = c->pinned;
+    c->pin_out = c->pin_in + mb * 8 + mb * kSlots + 1;
+    c->pin_pt = c->pin_out + mb * kSlots;
+    c->pin_one = c->pin_pt + (size_t)mb * p.max_pages_conv;
+    c->pin_zero = c->pin_one + 1;
+    c->pin_res = (double*)(c->pinned + ((c->pinned_ints + 1) & ~(size_t)1));
+    *c->pin_one = 1;
+    *c->pin_zero = 0;
+    build_dests(c);
+    // state region: zero (attention counters must start at 0)
+    HIPCHECK(hipMemsetAsync(c->ws + p.st_pos, 0, p.st_end - p.st_pos, c->stream));
+    HIPCHECK(hipMemcpyAsync(c->ws + p.meta_row0, p.emb_row0, sizeof p.emb_row0, hipMemcpyHostToDevice, c->stream));
+    HIPCHECK(hipMemcpyAsync(c->ws + p.meta_rows, p.emb_rows, sizeof p.emb_rows, hipMemcpyHostToDevice, c->stream));
+    launch_rope_table(c->at<float>(p.rope_t), cfg->ctx_max, cfg->d_t / cfg->n_heads_t, cfg->rope_base, c->stream);
+    launch_rope_table(c->at<float>(p.rope_d), cfg->n_q, cfg->d_d / cfg->n_heads_d, cfg->rope_base, c->stream);
+    HIPCHECK(hipGetLastError());
+    HIPCHECK(hipStreamSynchronize(c->stream));
+    c->pos_h.assign(mb, 0);
+    c->pages.assign(mb, {});
+    for (int i = p.n_pages - 1; i >= 0; --i) c->free_pages.push_back(i);
+    for (int b = 0; b < mb; ++b) reset_conv(c, b);
+  });
+  if (rc != MOSHI_OK) {
+    g_create_error = c->err;
+    moshi_destroy(c);
+    return rc;
+  }
+  *out = c;
+  return MOSHI_OK;
+}
+
+int moshi_init_weights(moshi_ctx* c, const moshi_tensor* t, int n) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    if (n < 0 || (n > 0 && !t)) fail(MOSHI_EINVAL, "bad tensor list");
+    const Plan& p = c->plan;
+    for (int i = 0; i < n; ++i) {
+      if (!t[i].name || !t[i].data) fail(MOSHI_EINVAL, "tensor %d has no name or data", i);
+      auto it = c->dests.find(t[i].name);
+      if (it == c->dests.end()) fail(MOSHI_EINVAL, "unknown tensor name '%s'", t[i].name);
+      Dest& ds = it->second;
+      if (t[i].numel != ds.rows * ds.cols)
+        fail(MOSHI_EINVAL, "tensor '%s' has %lld elements, %lld expected", t[i].name, (long long)t[i].numel,
+             ds.rows * ds.cols);
+      const bool bf = p.bf && !ds.f32;
+      void* dst = c->ws + ds.off;
+      if (t[i].on_device) {
+        launch_convert(t[i].data, ds.rows, ds.cols, dst, bf, ds.mult, ds.add, c->stream);
+        HIPCHECK(hipGetLastError());
+      } else {
+        const long long chunk_rows = std::max<long long>(1, (long long)(p.staging_bytes / 4) / ds.cols);
+        float* stg = c->at<float>(p.staging);
+        for (long long r0 = 0; r0 < ds.rows; r0 += chunk_rows) {
+          const long long nr = std::min(chunk_rows, ds.rows - r0);
+          HIPCHECK(hipMemcpyAsync(stg, t[i].data + r0 * ds.cols, (size_t)nr * ds.cols * 4, hipMemcpyHostToDevice,
+                                  c->stream));
+          launch_convert(stg, nr, ds.cols, dst, bf, ds.mult, ds.add + r0 * ds.mult, c->stream);
+          HIPCHECK(hipGetLastError());
+          HIPCHECK(hipStreamSynchronize(c->stream));
+        }
+      }
+      if (!ds.loaded) {
+        ds.loaded = true;
+        ++c->n_loaded;
+      }
+    }
+    HIPCHECK(hipStreamSynchronize(c->stream));
+    c->ready = c->n_loaded == c->dests.size();
+  });
+}
+
+int moshi_reset(moshi_ctx* c, int b) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    if (b < -1 || b >= c->cfg.max_batch) fail(MOSHI_EINVAL, "conversation %d out of range", b);
+    if (b == -1)
+      for (int i = 0; i < c->cfg.max_batch; ++i) reset_conv(c, i);
+    else
+      reset_conv(c, b);
+  });
+}
+
+int moshi_step(moshi_ctx* c, int32_t B, const int32_t* user, const int32_t* force, int32_t* out_tokens,
+               float* out_text, float* out_audio, int32_t flags) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    const moshi_config& g = c->cfg;
+    const Plan& p = c->plan;
+    if (!c->ready) fail(MOSHI_ESTATE, "weights not loaded");
+    if (B < 1 || B > g.max_batch) fail(MOSHI_EINVAL, "batch %d out of range 1..%d", B, g.max_batch);
+    if (!user || !out_tokens) fail(MOSHI_EINVAL, "user_codes and out_tokens are required");
+    for (int b = 0; b < B; ++b)
+      if (c->pos_h[b] + 1 > g.ctx_max) fail(MOSHI_ECONTEXT, "conversation %d is at ctx_max = %d", b, g.ctx_max);
+    const bool dev = flags & MOSHI_DEVICE_PTRS;
+    if (!dev) {
+      check_ids(user, (long long)B * 8, 8, 9, g);
+      if (force) check_ids(force, (long long)B * kSlots, kSlots, 0, g);
+    }
+    order_in(c);
+    for (int b = 0; b < B; ++b) ensure_pages(c, b, c->pos_h[b] + 1);
+    hipStream_t s = c->stream;
+    if (dev) {
+      HIPCHECK(hipMemcpyAsync(c->ws + p.st_user, user, (size_t)B * 8 * 4, hipMemcpyDeviceToDevice, s));
+      if (force)
+        HIPCHECK(hipMemcpyAsync(c->ws + p.st_force, force, (size_t)B * kSlots * 4, hipMemcpyDeviceToDevice, s));
+      HIPCHECK(hipMemcpyAsync(c->ws + p.st_has_force, force ? c->pin_one : c->pin_zero, 4, hipMemcpyHostToDevice, s));
+    } else {
+      HIPCHECK(hipStreamSynchronize(s));  // the pinned input block may still be in use
+      const int mb = g.max_batch;
+      memcpy(c->pin_in, user, (size_t)B * 8 * 4);
+      if (force) memcpy(c->pin_in + mb * 8, force, (size_t)B * kSlots * 4);
+      c->pin_in[mb * 8 + mb * kSlots] = force ? 1 : 0;
+      HIPCHECK(hipMemcpyAsync(c->ws + p.st_in, c->pin_in, (size_t)(mb * 8 + mb * kSlots + 1) * 4,
+                              hipMemcpyHostToDevice, s));
+    }
+    run_step(c, B, true);
+    const hipMemcpyKind k = dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
+    if (dev) {
+      HIPCHECK(hipMemcpyAsync(out_tokens, c->ws + p.st_out_tok, (size_t)B * kSlots * 4, k, s));
+    } else {
+      HIPCHECK(hipMemcpyAsync(c->pin_out, c->ws + p.st_out_tok, (size_t)B * kSlots * 4, k, s));
+    }
+    if (out_text) HIPCHECK(hipMemcpyAsync(out_text, c->ws + p.text_logits, (size_t)B * g.vocab_text * 4, k, s));
+    if (out_audio)
+      HIPCHECK(hipMemcpyAsync(out_audio, c->ws + p.audio_logits, (size_t)B * g.n_q * g.codebook * 4, k, s));
+    for (int b = 0; b < B; ++b) c->pos_h[b] += 1;
+    if (!dev) {
+      HIPCHECK(hipStreamSynchronize(s));
+      memcpy(out_tokens, c->pin_out, (size_t)B * kSlots * 4);
+    }
+    order_out(c);
+  });
+}
+
+int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B, int32_t S, int32_t flags,
+                                 float* text_logits, float* audio_logits, moshi_loss* loss) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    const moshi_config& g = c->cfg;
+    const Plan& p = c->plan;
+    if (!c->ready) fail(MOSHI_ESTATE, "weights not loaded");
+    if (!tokens) fail(MOSHI_EINVAL, "tokens are required");
+    if (B < 1 || B > g.max_batch) fail(MOSHI_EINVAL, "batch %d out of range 1..%d", B, g.max_batch);
+    const long long tf_max = g.max_tf_tokens ? g.max_tf_tokens : (long long)g.ctx_max * g.max_batch;
+    if (S < 1 || S > g.ctx_max) fail(MOSHI_EINVAL, "S = %d out of range 1..%d", S, g.ctx_max);
+    if ((long long)B * S > tf_max) fail(MOSHI_EINVAL, "B*S = %lld exceeds max_tf_tokens %lld", (long long)B * S, tf_max);
+    for (int b = 0; b < B; ++b)
+      if (c->pos_h[b] != 0) fail(MOSHI_ESTATE, "conversation %d is not at position 0", b);
+    const bool dev = flags & MOSHI_DEVICE_PTRS;
+    const bool depth = !(flags & MOSHI_TF_SKIP_DEPTH);
+    if (!dev) check_ids(tokens, (long long)B * S * kStreams, kStreams, 0, g);
+    order_in(c);
+    hipStream_t s = c->stream;
+    const int* tok = tokens;
+    if (!dev) {
+      HIPCHECK(hipMemcpyAsync(c->ws + p.tf_tokens, tokens, (size_t)B * S * kStreams * 4, hipMemcpyHostToDevice, s));
+      tok = c->at<int>(p.tf_tokens);
+    }
+    for (int b = 0; b < B; ++b) ensure_pages(c, b, S);
+    HIPCHECK(hipMemcpyAsync(c->ws + p.st_has_force, c->pin_one, 4, hipMemcpyHostToDevice, s));
+    const hipMemcpyKind k = dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
+    for (int st = 0; st < S; ++st) {
+      HIPCHECK(hipMemcpy2DAsync(c->ws + p.st_user, 8 * 4, tok + (size_t)st * kStreams + kSlots,
+                                (size_t)S * kStreams * 4, 8 * 4, B, hipMemcpyDeviceToDevice, s));
+      HIPCHECK(hipMemcpy2DAsync(c->ws + p.st_force, kSlots * 4, tok + (size_t)st * kStreams,
+                                (size_t)S * kStreams * 4, kSlots * 4, B, hipMemcpyDeviceToDevice, s));
+      run_step(c, B, depth);
+      if (text_logits)
+        HIPCHECK(hipMemcpy2DAsync(text_logits + (size_t)st * g.vocab_text, (size_t)S * g.vocab_text * 4,
+                                  c->ws + p.text_logits, (size_t)g.vocab_text * 4, (size_t)g.vocab_text * 4, B, k, s));
+      if (audio_logits && depth) {
+        const size_t row = (size_t)g.n_q * g.codebook;
+        HIPCHECK(hipMemcpy2DAsync(audio_logits + (size_t)st * row, (size_t)S * row * 4, c->ws + p.audio_logits,
+                                  row * 4, row * 4, B, k, s));
+      }
+      if (loss) {
+        CeRowsArgs ca{};
+        ca.text_logits = c->at<float>(p.text_logits);
+        ca.ld_text = g.vocab_text;
+        ca.audio_logits = c->at<float>(p.audio_logits);
+        ca.ld_audio = (long long)g.n_q * g.codebook;
+        ca.targets = c->at<int>(p.st_force);
+        ca.tgt_stride = kSlots;
+        ca.vocab_text = g.vocab_text;
+        ca.codebook = g.codebook;
+        ca.ce = c->at<double>(p.tf_ce);
+        ca.S = S;
+        ca.s = st;
+        launch_ce_rows(ca, B, depth, s);
+        HIPCHECK(hipGetLastError());
+      }
+    }
+    for (int b = 0; b < B; ++b) c->pos_h[b] = S;
+    if (loss) {
+      launch_ce_reduce(c->at<double>(p.tf_ce), (long long)B * S, depth ? kSlots : 1, c->at<double>(p.tf_res), s);
+      HIPCHECK(hipGetLastError());
+      HIPCHECK(hipMemcpyAsync(c->pin_res, c->ws + p.tf_res, 20 * 8, hipMemcpyDeviceToHost, s));
+    }
+    HIPCHECK(hipStreamSynchronize(s));
+    if (loss) {
+      const double* r = c->pin_res;
+      loss->ce_text = r[0];
+      for (int j = 0; j < 8; ++j) loss->ce_per_cb[j] = r[1 + j];
+      loss->n_text = (int64_t)r[kSlots];
+      long long na = 0;
+      for (int j = 1; j < kSlots; ++j) na += (long long)r[kSlots + j];
+      loss->n_audio = na;
+      loss->ce_audio = r[18];
+      loss->ce_total = r[19];
+    }
+    if (!(flags & MOSHI_TF_FILL_KV))
+      for (int b = 0; b < B; ++b) reset_conv(c, b);
+    order_out(c);
+  });
+}
+
+int moshi_sync(moshi_ctx* c) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    HIPCHECK(hipStreamSynchronize(c->stream));
+    int e = 0;
+    HIPCHECK(hipMemcpy(&e, c->ws + c->plan.st_err, 4, hipMemcpyDeviceToHost));
+    if (e) {
+      int zero = 0;
+      HIPCHECK(hipMemcpy(c->ws + c->plan.st_err, &zero, 4, hipMemcpyHostToDevice));
+      fail(MOSHI_EINVAL, "a token id outside [0, pad] reached the device (replaced by pad)");
+    }
+  });
+}
+
+int moshi_position(const moshi_ctx* c, int b) {
+  if (!c || b < 0 || b >= c->cfg.max_batch) return MOSHI_EINVAL;
+  return c->pos_h[b];
+}
+
+int moshi_delay_codes(const int32_t* frames, int32_t T, int32_t tau, int32_t pad, int32_t* out) {
+  if (T < 0 || tau < 0 || (T > 0 && (!frames || !out))) return MOSHI_EINVAL;
+  for (int s = 0; s < T; ++s) {
+    out[s * 8] = frames[s * 8];
+    for (int q = 1; q < 8; ++q) out[s * 8 + q] = s - tau >= 0 ? frames[(s - tau) * 8 + q] : pad;
+  }
+  return MOSHI_OK;
+}
+
+int moshi_undelay_codes(const int32_t* model, int32_t T, int32_t tau, int32_t* out) {
+  if (T < 0 || tau < 0 || (T > tau && (!model || !out))) return MOSHI_EINVAL;
+  for (int t = 0; t + tau < T; ++t) {
+    out[t * 8] = model[t * 8];
+    for (int q = 1; q < 8; ++q) out[t * 8 + q] = model[(t + tau) * 8 + q];
+  }
+  return MOSHI_OK;
+}
+
+const char* moshi_last_error(const moshi_ctx* c) { return c ? c->err.c_str() : g_create_error.c_str(); }
+
+void moshi_destroy(moshi_ctx* c) {
+  if (!c) return;
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  if (c->pinned) (void)hipHostFree(c->pinned);
+  if (c->ev_in) (void)hipEventDestroy(c->ev_in);
+  if (c->ev_out) (void)hipEventDestroy(c->ev_out);
+  if (c->stream) (void)hipStreamDestroy(c->stream);
+  delete c;
+}
+
+}  // extern "C"

@@ -1,0 +1,530 @@
+// gfx950 kernels of the streaming frame step (batch 1..8).
+//
+// The step follows the RQ-Transformer of the Moshi paper walkthrough on
+// 139.9.1.231 (section "使用 RQ-Transformer 的分层自回归建模", Fig. 3): a
+// Helium-style Temporal Transformer ("Helium 文本语言模型 / 架构": RMSNorm at
+// the attention, feed-forward and output-linear inputs, RoPE, causal attention,
+// SiLU-gated linear unit) advances one position per frame, then a Depth
+// Transformer with per-index weights produces Moshi's codebooks in order.
+//
+// At batch <= 8 every linear map is a weight-streaming matrix-vector product:
+// HBM-bound, so the kernels are built around wide coalesced weight loads, not
+// matrix cores.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "moshi_internal.h"
+
+namespace moshi {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// float -> bfloat16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// 16 bytes of weights -> EPL floats. Weights are read once per frame, so the
+// loads are non-temporal.
+template <bool BF>
+struct WLoad;
+template <>
+struct WLoad<true> {
+  static constexpr int EPL = 8;
+  __device__ __forceinline__ static void get(const void* base, long long idx, float (&w)[8]) {
+    u32x4 v = __builtin_nontemporal_load((const u32x4*)((const uint16_t*)base + idx));
+    w[0] = bf_lo(v.x); w[1] = bf_hi(v.x); w[2] = bf_lo(v.y); w[3] = bf_hi(v.y);
+    w[4] = bf_lo(v.z); w[5] = bf_hi(v.z); w[6] = bf_lo(v.w); w[7] = bf_hi(v.w);
+  }
+};
+template <>
+struct WLoad<false> {
+  static constexpr int EPL = 4;
+  __device__ __forceinline__ static void get(const void* base, long long idx, float (&w)[4]) {
+    f32x4 v = __builtin_nontemporal_load((const f32x4*)((const float*)base + idx));
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+};
+
+__device__ __forceinline__ float load_w1(const void* base, long long idx, bool bf) {
+  return bf ? bf2f(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
+}
+
+// ---------------------------------------------------------------------------
+// y = W * f(x) for NB input vectors; f = RMSNorm(.) * gain when gain != null.
+// Block: 4 waves, each owning 4 consecutive output rows (so RoPE and SwiGLU
+// pairs (2i, 2i+1) stay inside one wave). The normalised inputs are staged in
+// LDS in K-chunks of KC elements; each lane streams 16-byte weight pieces and
+// the wave reduces its rows with cross-lane shuffles.
+// ---------------------------------------------------------------------------
+constexpr int kGemvRowsPerWave = 4;
+constexpr int kGemvRows = 4 * kGemvRowsPerWave;
+constexpr int kGemvLdsFloats = 16384;
+
+template <int NB, bool BF, int EPI>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a, int KC) {
+  constexpr int EPL = WLoad<BF>::EPL;
+  constexpr int RPW = kGemvRowsPerWave;
+  extern __shared__ float xs[];  // [NB][kn]
+  __shared__ float s_red[4][NB];
+  __shared__ float s_rstd[NB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+
+  if (a.gain) {
+    float ss[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) ss[b] = 0.f;
+    for (int k = tid; k < K; k += 256) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float v = a.x[(long long)b * a.ldx + k];
+        ss[b] += v * v;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      ss[b] = wave_sum(ss[b]);
+      if (lane == 0) s_red[wave][b] = ss[b];
+    }
+    __syncthreads();
+    if (tid < NB) {
+      float t = s_red[0][tid] + s_red[1][tid] + s_red[2][tid] + s_red[3][tid];
+      s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+
+  const int row0 = blockIdx.x * kGemvRows + wave * RPW;
+  float acc[RPW][NB];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  for (int kc0 = 0; kc0 < K; kc0 += KC) {
+    const int kn = min(KC, K - kc0);
+    if (kc0) __syncthreads();
+    for (int i = tid * 4; i < NB * kn; i += 1024) {
+      const int b = i / kn, k = i - b * kn;
+      float4 v = *(const float4*)(a.x + (long long)b * a.ldx + kc0 + k);
+      if (a.gain) {
+        const float r = s_rstd[b];
+        const float4 g = *(const float4*)(a.gain + kc0 + k);
+        v.x *= r * g.x; v.y *= r * g.y; v.z *= r * g.z; v.w *= r * g.w;
+      }
+      *(float4*)(xs + i) = v;
+    }
+    __syncthreads();
+#pragma unroll 2
+    for (int kk = lane * EPL; kk < kn; kk += 64 * EPL) {
+      float w[RPW][EPL];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if (row0 + r < N) {
+          WLoad<BF>::get(a.W, (long long)(row0 + r) * K + kc0 + kk, w[r]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) w[r][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float xv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+          const float4 t = *(const float4*)(xs + b * kn + kk + e);
+          xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+        }
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[r][b] = fmaf(w[r][e], xv[e], acc[r][b]);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+  if (lane != 0) return;
+
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float* y = a.y + (long long)b * a.ldy;
+    if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int row = row0 + r;
+        if (row >= N) break;
+        float s = acc[r][b];
+        if (EPI == EPI_RESID) s += y[row];
+        if (EPI == EPI_EMB) {
+          const int t = min(max(a.tok[b * a.tok_stride + a.tok_col], 0), a.tok_rows - 1);
+          s += load_w1(a.emb, (long long)t * N + row, BF);
+        }
+        y[row] = s;
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // rows (2i, 2i+1) = (gate_i, up_i)
+#pragma unroll
+      for (int r = 0; r < RPW; r += 2) {
+        const int row = row0 + r;
+        if (row + 1 >= N) break;
+        const float g = acc[r][b], u = acc[r + 1][b];
+        y[row >> 1] = g / (1.0f + expf(-g)) * u;
+      }
+    } else if constexpr (EPI == EPI_QKV) {
+      const int p = a.pos ? a.pos[b] : a.pos_const;
+#pragma unroll
+      for (int r = 0; r < RPW; r += 2) {
+        const int row = row0 + r;
+        if (row + 1 >= N) break;
+        float x0 = acc[r][b], x1 = acc[r + 1][b];
+        const int part = row / a.d;  // 0 q, 1 k, 2 v
+        const int rr = row - part * a.d;
+        const int head = rr / a.hd, dim = rr - head * a.hd;
+        if (part < 2) {
+          const float* cs = a.rope + ((long long)p * (a.hd >> 1) + (dim >> 1)) * 2;
+          const float c = cs[0], sn = cs[1];
+          const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+          x0 = y0; x1 = y1;
+        }
+        if (part == 0) {
+          y[rr] = x0;
+          y[rr + 1] = x1;
+        } else {
+          const long long off = a.kv.offset(b, a.layer, part - 1, head, p) + dim;
+          if (a.kv_bf16) {
+            uint16_t* kv = (uint16_t*)a.kv.base;
+            kv[off] = f2bf(x0);
+            kv[off + 1] = f2bf(x1);
+          } else {
+            float* kv = (float*)a.kv.base;
+            kv[off] = x0;
+            kv[off + 1] = x1;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int NB, bool BF>
+static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s) {
+  dim3 grid((a.N + kGemvRows - 1) / kGemvRows);
+  size_t lds = (size_t)NB * (size_t)KC * sizeof(float);
+  switch (epi) {
+    case EPI_STORE: k_gemv<NB, BF, EPI_STORE><<<grid, 256, lds, s>>>(a, KC); break;
+    case EPI_RESID: k_gemv<NB, BF, EPI_RESID><<<grid, 256, lds, s>>>(a, KC); break;
+    case EPI_EMB: k_gemv<NB, BF, EPI_EMB><<<grid, 256, lds, s>>>(a, KC); break;
+    case EPI_SWIGLU: k_gemv<NB, BF, EPI_SWIGLU><<<grid, 256, lds, s>>>(a, KC); break;
+    case EPI_QKV: k_gemv<NB, BF, EPI_QKV><<<grid, 256, lds, s>>>(a, KC); break;
+  }
+}
+
+template <bool BF>
+static void gemv_dispatch(const GemvArgs& a, int B, int epi, hipStream_t s) {
+  constexpr int span = 64 * WLoad<BF>::EPL;
+  const int cap = kGemvLdsFloats / B;
+  int KC = a.K <= cap ? a.K : (cap / span) * span;
+  switch (B) {
+    case 1: gemv_dispatch_epi<1, BF>(a, epi, KC, s); break;
+    case 2: gemv_dispatch_epi<2, BF>(a, epi, KC, s); break;
+    case 3: gemv_dispatch_epi<3, BF>(a, epi, KC, s); break;
+    case 4: gemv_dispatch_epi<4, BF>(a, epi, KC, s); break;
+    case 5: gemv_dispatch_epi<5, BF>(a, epi, KC, s); break;
+    case 6: gemv_dispatch_epi<6, BF>(a, epi, KC, s); break;
+    case 7: gemv_dispatch_epi<7, BF>(a, epi, KC, s); break;
+    case 8: gemv_dispatch_epi<8, BF>(a, epi, KC, s); break;
+  }
+}
+
+void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s) {
+  if (bf16)
+    gemv_dispatch<true>(a, B, epi, s);
+  else
+    gemv_dispatch<false>(a, B, epi, s);
+}
+
+// ---------------------------------------------------------------------------
+// Causal decode attention, split over key blocks (flash-decode). Block
+// (split, head, conversation) scores up to 64 keys of one KV page with a
+// group of HD/EPL lanes per key (each lane holds EPL query values), keeps the
+// probabilities in LDS, and accumulates P*V in the same lane layout. Each
+// block writes (o, max, sum) for its split; the last block of a (b, head) to
+// finish, found with an atomic counter, merges the splits in split order, so
+// the result does not depend on block timing.
+// ---------------------------------------------------------------------------
+template <bool KBF, int HD>
+__global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
+  constexpr int EPL = KBF ? 8 : 4;
+  constexpr int G = HD / EPL;  // lanes per key
+  constexpr int KPW = 64 / G;  // keys per wave per pass
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = gridDim.y;
+  const int P = (a.pos ? a.pos[b] : a.pos_const) + 1;
+  const int nact = (P + a.split - 1) / a.split;
+  if (sp >= nact) return;
+  const int k0 = sp * a.split, k1 = min(P, k0 + a.split), n = k1 - k0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane % G, g = lane / G;
+  __shared__ float sc[64];
+  __shared__ float so[4 * KPW * HD];
+  __shared__ float s_ml[2];
+  __shared__ int s_last;
+
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = a.q[(long long)b * a.ldq + h * HD + li * EPL + e] * a.scale;
+
+  for (int base = k0 + wave * KPW; base < k1; base += 4 * KPW) {
+    const int key = base + g;
+    float d = 0.f;
+    if (key < k1) {
+      const long long off = a.kv.offset(b, a.layer, 0, h, key) + li * EPL;
+      float kf[EPL];
+      if constexpr (KBF) {
+        u32x4 v = *(const u32x4*)((const uint16_t*)a.kv.base + off);
+        kf[0] = bf_lo(v.x); kf[1] = bf_hi(v.x); kf[2] = bf_lo(v.y); kf[3] = bf_hi(v.y);
+        kf[4] = bf_lo(v.z); kf[5] = bf_hi(v.z); kf[6] = bf_lo(v.w); kf[7] = bf_hi(v.w);
+      } else {
+        f32x4 v = *(const f32x4*)((const float*)a.kv.base + off);
+        kf[0] = v.x; kf[1] = v.y; kf[2] = v.z; kf[3] = v.w;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], kf[e], d);
+    }
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+    if (key < k1 && li == 0) sc[key - k0] = d;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float s = lane < n ? sc[lane] : -INFINITY;
+    const float m = wave_max(s);
+    const float p = lane < n ? expf(s - m) : 0.f;
+    const float l = wave_sum(p);
+    if (lane < n) sc[lane] = p;
+    if (lane == 0) {
+      s_ml[0] = m;
+      s_ml[1] = l;
+    }
+  }
+  __syncthreads();
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int base = k0 + wave * KPW; base < k1; base += 4 * KPW) {
+    const int key = base + g;
+    if (key < k1) {
+      const float p = sc[key - k0];
+      const long long off = a.kv.offset(b, a.layer, 1, h, key) + li * EPL;
+      float vf[EPL];
+      if constexpr (KBF) {
+        u32x4 v = *(const u32x4*)((const uint16_t*)a.kv.base + off);
+        vf[0] = bf_lo(v.x); vf[1] = bf_hi(v.x); vf[2] = bf_lo(v.y); vf[3] = bf_hi(v.y);
+        vf[4] = bf_lo(v.z); vf[5] = bf_hi(v.z); vf[6] = bf_lo(v.w); vf[7] = bf_hi(v.w);
+      } else {
+        f32x4 v = *(const f32x4*)((const float*)a.kv.base + off);
+        vf[0] = v.x; vf[1] = v.y; vf[2] = v.z; vf[3] = v.w;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) so[(wave * KPW + g) * HD + li * EPL + e] = acc[e];
+  __syncthreads();
+
+  float* part = a.part + ((long long)(b * H + h) * a.max_splits) * (HD + 2);
+  if (tid < HD) {
+    float o = 0.f;
+    for (int i = 0; i < 4 * KPW; ++i) o += so[i * HD + tid];
+    part[(long long)sp * (HD + 2) + tid] = o;
+    if (tid == 0) {
+      part[(long long)sp * (HD + 2) + HD] = s_ml[0];
+      part[(long long)sp * (HD + 2) + HD + 1] = s_ml[1];
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(&a.counters[b * H + h], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (old == nact - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (tid < HD) {
+    float M = -INFINITY;
+    for (int i = 0; i < nact; ++i)
+      M = fmaxf(M, __hip_atomic_load(part + (long long)i * (HD + 2) + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float L = 0.f, o = 0.f;
+    for (int i = 0; i < nact; ++i) {
+      const float* pi = part + (long long)i * (HD + 2);
+      const float w = expf(__hip_atomic_load(pi + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
+      L = fmaf(w, __hip_atomic_load(pi + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), L);
+      o = fmaf(w, __hip_atomic_load(pi + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), o);
+    }
+    a.out[(long long)b * a.ldo + h * HD + tid] = o / L;
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[b * H + h], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s) {
+  dim3 grid(a.max_splits, H, B);
+#define MOSHI_ATTN(KB, HDV) k_attn_decode<KB, HDV><<<grid, 256, 0, s>>>(a)
+  if (kv_bf16) {
+    if (hd == 32) MOSHI_ATTN(true, 32);
+    else if (hd == 64) MOSHI_ATTN(true, 64);
+    else MOSHI_ATTN(true, 128);
+  } else {
+    if (hd == 32) MOSHI_ATTN(false, 32);
+    else if (hd == 64) MOSHI_ATTN(false, 64);
+    else MOSHI_ATTN(false, 128);
+  }
+#undef MOSHI_ATTN
+}
+
+// ---------------------------------------------------------------------------
+// Temporal input: the sum of the 17 sub-streams' embedding rows of the
+// previous frame (walkthrough, "使用 RQ-Transformer ...": the input of step s
+// is the sum of K learnt embedding tables of V_{s-1}).
+// ---------------------------------------------------------------------------
+template <bool BF>
+__global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.d) return;
+  float s = 0.f;
+  for (int k = 0; k < kStreams; ++k) {
+    int t = a.frames[b * kStreams + k];
+    if (t < 0 || t >= a.rows[k]) {
+      if (i == 0) atomicOr(a.err, 1);
+      t = a.rows[k] - 1;
+    }
+    const long long idx = (a.row0[k] + t) * (long long)a.d + i;
+    s += BF ? bf2f(((const uint16_t*)a.table)[idx]) : ((const float*)a.table)[idx];
+  }
+  a.h[(long long)b * a.d + i] = s;
+}
+
+void launch_embed(const EmbedArgs& a, int B, bool bf16, hipStream_t s) {
+  dim3 grid((a.d + 255) / 256, B);
+  if (bf16)
+    k_embed<true><<<grid, 256, 0, s>>>(a);
+  else
+    k_embed<false><<<grid, 256, 0, s>>>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Greedy choice: argmax with the lowest index winning ties.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_argmax(ArgmaxArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* l = a.logits + (long long)b * a.ld;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = tid; i < a.n; i += 256) {
+    const float v = l[i];
+    if (v > bv) {
+      bv = v;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if (lane == 0) {
+    sv[wave] = bv;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
+    int own = (bi == 0x7fffffff) ? 0 : bi;
+    if (a.pad_after && a.pos[b] < a.delay) own = a.pad_id;
+    a.out_tok[b * kSlots + a.slot] = own;
+    a.cur_tok[b * kSlots + a.slot] = *a.has_force ? a.force[b * kSlots + a.slot] : own;
+  }
+}
+
+void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s) { k_argmax<<<B, 256, 0, s>>>(a); }
+
+// ---------------------------------------------------------------------------
+// End of a frame: V_s = (Moshi's slots fed forward) ++ (user's slots) becomes
+// the next input; the position advances.
+// ---------------------------------------------------------------------------
+__global__ void k_advance(AdvanceArgs a, int B) {
+  const int t = threadIdx.x;
+  if (t < B * kStreams) {
+    const int b = t / kStreams, k = t - b * kStreams;
+    int v = k >= kSlots ? a.user[b * 8 + (k - kSlots)]
+                        : (*a.has_force ? a.force[b * kSlots + k] : a.cur_tok[b * kSlots + k]);
+    const int hi = k == 0 ? a.pad_text : a.pad_audio;
+    if (v < 0 || v > hi) {
+      atomicOr(a.err, 1);
+      v = hi;
+    }
+    a.prev[b * kStreams + k] = v;
+  }
+  __syncthreads();
+  if (t < B) a.pos[t] += 1;
+}
+
+void launch_advance(const AdvanceArgs& a, int B, hipStream_t s) { k_advance<<<1, 256, 0, s>>>(a, B); }
+
+// ---------------------------------------------------------------------------
+// Weight repack: float32 rows -> destination rows r*mult + add (float32 or bf16).
+// ---------------------------------------------------------------------------
+__global__ void k_convert(const float* src, long long rows, int cols, void* dst, int bf, long long mult,
+                          long long add) {
+  const long long total = rows * cols;
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+    const long long r = i / cols, c = i - r * cols;
+    const long long o = (r * mult + add) * cols + c;
+    if (bf)
+      ((uint16_t*)dst)[o] = f2bf(src[i]);
+    else
+      ((float*)dst)[o] = src[i];
+  }
+}
+
+void launch_convert(const float* src, long long rows, int cols, void* dst, bool bf16, long long mult, long long add,
+                    hipStream_t s) {
+  long long total = rows * cols;
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  k_convert<<<(unsigned)blocks, 256, 0, s>>>(src, rows, cols, dst, bf16 ? 1 : 0, mult, add);
+}
+
+}  // namespace moshi

@@ -1,0 +1,132 @@
+// Internal interfaces between the host engine and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moshi {
+
+constexpr int kMaxBatch = 8;
+constexpr int kSlots = 9;     // Moshi's own slots per frame: text + 8 codebooks
+constexpr int kStreams = 17;  // slots per frame
+
+// Location of one key/value vector in a paged cache. A page holds `pf`
+// consecutive positions of one conversation for every layer, laid out
+// [layer][k|v][head][pos_in_page][hd]. Without a page table page = b.
+struct KvView {
+  void* base;
+  const int* page_table;  // [B][pt_stride] physical page per logical page, or null
+  int pt_stride;
+  long long page_stride;  // elements per page
+  int pf;                 // positions per page
+  int n_heads;
+  int hd;
+  __device__ __forceinline__ long long offset(int b, int layer, int kv, int head, int p) const {
+    int page = page_table ? page_table[b * pt_stride + p / pf] : b;
+    return (long long)page * page_stride +
+           ((long long)((layer * 2 + kv) * n_heads + head) * pf + (p % pf)) * hd;
+  }
+};
+
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_EMB = 2, EPI_SWIGLU = 3, EPI_QKV = 4 };
+
+struct GemvArgs {
+  const void* W;  // [N][K] row-major, float or bf16 bits
+  int N, K;
+  const float* x;  // [B][ldx]
+  int ldx;
+  const float* gain;  // RMSNorm gain of x, or null (no normalisation)
+  float eps;
+  float* y;  // [B][ldy]
+  int ldy;
+  // EPI_QKV
+  const int* pos;  // [B] positions, or null -> pos_const
+  int pos_const;
+  const float* rope;  // [positions][hd/2][cos, sin]
+  int hd, d;          // head dim and model dim (q | k | v row boundaries)
+  KvView kv;
+  int kv_bf16;
+  int layer;
+  // EPI_EMB: y = W x + emb[tok[b * tok_stride + tok_col]]
+  const void* emb;
+  const int* tok;
+  int tok_stride, tok_col;
+  int tok_rows;  // rows of emb (ids are clamped into range)
+};
+
+struct AttnArgs {
+  const float* q;  // [B][ldq], head h at h*hd
+  int ldq;
+  KvView kv;
+  int layer;
+  const int* pos;  // [B]: keys 0..pos[b]; null -> pos_const
+  int pos_const;
+  int split;       // keys per block (<= 64)
+  float* part;     // [B][H][max_splits][hd + 2]
+  int max_splits;
+  int* counters;   // [B][H], zero between uses
+  float* out;      // [B][ldo]
+  int ldo;
+  float scale;
+};
+
+struct EmbedArgs {
+  const void* table;       // 17 tables back to back, rows of d elements
+  const long long* row0;   // [17] first row of each table
+  const int* rows;         // [17] rows of each table (pad row included)
+  const int* frames;       // [B][17]
+  float* h;                // [B][d]
+  int d;
+  int* err;
+};
+
+struct ArgmaxArgs {
+  const float* logits;  // [B][ld]
+  int n, ld;
+  int slot;
+  int pad_after;   // pad the slot while pos[b] < delay (acoustic slots)
+  int pad_id, delay;
+  const int* pos;
+  int* out_tok;    // [B][9] own tokens
+  int* cur_tok;    // [B][9] tokens fed forward (forced or own)
+  const int* force;      // [B][9]
+  const int* has_force;  // scalar flag
+};
+
+struct AdvanceArgs {
+  const int* cur_tok;  // [B][9]
+  const int* force;      // [B][9], used instead of cur_tok when *has_force
+  const int* has_force;
+  const int* user;     // [B][8]
+  int* prev;           // [B][17]
+  int* pos;            // [B]
+  int* err;
+  int pad_text, pad_audio;
+};
+
+struct CeRowsArgs {
+  const float* text_logits;   // [B][ld_text]
+  long long ld_text;
+  const float* audio_logits;  // [B][ld_audio] = [B][8][codebook]
+  long long ld_audio;
+  const int* targets;         // [B][tgt_stride], slots 0..8
+  int tgt_stride;
+  int vocab_text, codebook;
+  double* ce;                 // [B][S][9]
+  int S, s;
+};
+
+// launchers (kernels_decode.hip)
+void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s);
+void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s);
+void launch_embed(const EmbedArgs& a, int B, bool bf16, hipStream_t s);
+void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s);
+void launch_advance(const AdvanceArgs& a, int B, hipStream_t s);
+void launch_convert(const float* src, long long rows, int cols, void* dst, bool bf16, long long dst_row_mult,
+                    long long dst_row_add, hipStream_t s);
+// launchers (kernels_loss.hip)
+void launch_ce_rows(const CeRowsArgs& a, int B, bool with_audio, hipStream_t s);
+void launch_ce_reduce(const double* ce, long long n_rows, int n_slots, double* res, hipStream_t s);
+void launch_rope_table(float* out, int P, int hd, double base, hipStream_t s);
+
+}  // namespace moshi

@@ -1,0 +1,184 @@
+/*
+ * moshi.h -- C ABI of the MI355X (gfx950) RQ-Transformer frame-step library.
+ *
+ * The library runs Moshi's per-frame RQ-Transformer step and its teacher-forced
+ * scoring pass on one GPU. Terms and equations refer to these web pages:
+ *   [W] the Chinese walkthrough of the Moshi technical report on 139.9.1.231
+ *       (sections "使用 RQ-Transformer 的分层自回归建模" with Fig. 3,
+ *       "音频建模 / 声学延迟" with eq. 4, "多流建模", "内心独白",
+ *       "Moshi的联合序列建模" with eq. 6 and Fig. 4, "训练损失",
+ *       "Helium 文本语言模型 / 架构");
+ *   [N] the notes page "Moshi: a Speech-Text Foundation Model for Real-Time
+ *       Dialogue" (sections 3b, 3c, 3d and 4).
+ *
+ * Token layout ("model order"): every frame holds K = 2*n_q + 1 = 17 ids
+ * (eq. 6 / Fig. 4 of [W]): slot 0 the text token (Inner Monologue), slots
+ * 1..8 Moshi's codebooks (1 semantic, 2..8 acoustic, delayed by `delay`
+ * frames), slots 9..16 the user's codebooks in the same delayed order. The pad
+ * id of the text slot is vocab_text, of audio slots codebook; pad marks an
+ * absent token (the initial frame, delayed codebooks before the first frame).
+ *
+ * Conventions for every call:
+ *   - return 0 (MOSHI_OK) or a negative MOSHI_E* code; moshi_last_error()
+ *     gives a message. On error the context's state is unchanged.
+ *   - pointers are host memory unless the call's flags include
+ *     MOSHI_DEVICE_PTRS; host buffers are read/written only during the call.
+ *   - calls on one context are not thread-safe.
+ *   - all GPU work runs on a stream owned by the context; when a caller
+ *     stream was given to moshi_create, every call is ordered after the work
+ *     already queued on it and the caller stream waits for the call's work.
+ */
+#ifndef MOSHI_H
+#define MOSHI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MOSHI_OK 0
+#define MOSHI_EINVAL (-1)   /* bad config, shape, pointer or token id */
+#define MOSHI_ECONTEXT (-2) /* the step would exceed ctx_max positions */
+#define MOSHI_ENOMEM (-3)   /* workspace too small or no free KV page */
+#define MOSHI_EHIP (-4)     /* HIP runtime error (message has the HIP string) */
+#define MOSHI_ESTATE (-5)   /* call not valid in this state (e.g. no weights) */
+
+/* weight precision (moshi_config.dtype) */
+#define MOSHI_F32 0
+#define MOSHI_BF16 1
+
+/* flags */
+#define MOSHI_DEVICE_PTRS 1   /* all array arguments are device pointers; the call
+                                 only enqueues work (see moshi_sync) */
+#define MOSHI_TF_FILL_KV 2    /* teacher-forced: keep the KV cache and continue
+                                 streaming at frame S+1 */
+#define MOSHI_TF_SKIP_DEPTH 4 /* teacher-forced: temporal pass and text only */
+
+/* Model and capacity description. Shapes follow [W] "使用 RQ-Transformer ..."
+ * (Temporal Transformer with the Helium architecture, Depth Transformer with
+ * one weight set per codebook index) and [N] 3b/3c. */
+typedef struct moshi_config {
+  int32_t d_t, n_layers_t, n_heads_t, ffn_t; /* temporal width, layers, heads, SwiGLU hidden */
+  int32_t ctx_max;                           /* max positions per conversation */
+  int32_t d_d, n_layers_d, n_heads_d, ffn_d; /* depth width, layers, heads, SwiGLU hidden */
+  int32_t vocab_text;                        /* text vocabulary (pad id = vocab_text) */
+  int32_t codebook;                          /* codebook size N_A (pad id = codebook) */
+  int32_t n_q;                               /* codebooks per speaker; must be 8 */
+  int32_t delay;                             /* acoustic delay tau, in frames (>= 0) */
+  float rope_base, norm_eps;                 /* RoPE base, RMSNorm epsilon */
+  int32_t dtype;                             /* MOSHI_F32 or MOSHI_BF16 weights */
+  int32_t max_batch;                         /* conversations per context (1..8) */
+  int32_t page_frames;                       /* KV page size in frames (64) */
+  int32_t n_pages;                           /* KV pages in the pool; 0 = max_batch*ceil(ctx_max/page_frames) */
+  int32_t max_tf_tokens;                     /* max B*S of moshi_forward_teacher_forced (0 = ctx_max*max_batch) */
+} moshi_config;
+
+/* One weight tensor handed to moshi_init_weights: float32, C-order. Names and
+ * shapes ([out, in] for linear maps, [rows, dim] for embedding tables with the
+ * pad row last):
+ *   temporal.emb.{k}                k = 0..16, rows vocab_text+1 (k = 0) or codebook+1
+ *   temporal.layers.{l}.{attn_norm,ffn_norm}            [d_t]
+ *   temporal.layers.{l}.{wq,wk,wv,wo}                   [d_t, d_t]
+ *   temporal.layers.{l}.{w_gate,w_up}                   [ffn_t, d_t]
+ *   temporal.layers.{l}.w_down                          [d_t, ffn_t]
+ *   temporal.out_norm [d_t], temporal.text_head [vocab_text, d_t]
+ *   depth.{j}.in_proj [d_d, d_t], depth.{j}.emb rows vocab_text+1 (j = 0) or codebook+1
+ *   depth.{j}.layers.{l}.* as for the temporal layers with d_d, ffn_d
+ *   depth.{j}.out_norm [d_d], depth.{j}.head [codebook, d_d]       j = 0..7
+ */
+typedef struct moshi_tensor {
+  const char* name;
+  const float* data;
+  int64_t numel;
+  int32_t on_device; /* 1: data is a device pointer */
+  int32_t reserved;
+} moshi_tensor;
+
+/* Cross-entropy of the teacher-forced pass ([W] "训练损失"; weights of [N] 4):
+ * ce_text over the text slot; ce_per_cb[j] over Moshi's codebook j; ce_audio =
+ * sum_j alpha_j ce_per_cb[j] / sum_j alpha_j with alpha = (100, 1, ..., 1);
+ * ce_total = ce_text + ce_audio. Pad targets are excluded from every mean. */
+typedef struct moshi_loss {
+  double ce_text, ce_audio, ce_total;
+  double ce_per_cb[8];
+  int64_t n_text, n_audio;
+} moshi_loss;
+
+typedef struct moshi_ctx moshi_ctx;
+
+/* Bytes of device workspace the context needs for `cfg` (0 if cfg is invalid). */
+size_t moshi_workspace_bytes(const moshi_config* cfg);
+
+/* Validate cfg; returns MOSHI_OK or MOSHI_EINVAL with a message in msg. */
+int moshi_check_config(const moshi_config* cfg, char* msg, size_t msg_len);
+
+/* Create a context on the current HIP device. `workspace` is caller-owned
+ * device memory of at least moshi_workspace_bytes(cfg) bytes that outlives the
+ * context; the library keeps weights, KV pages and activations in it.
+ * `hip_stream` (may be NULL) is the caller's stream, see the conventions. */
+int moshi_create(const moshi_config* cfg, void* hip_stream, void* workspace, size_t ws_bytes,
+                 moshi_ctx** out);
+
+/* Copy and repack weights (float32 in, converted to cfg.dtype). Every tensor
+ * listed above must be given exactly once over one or more calls; the
+ * context becomes usable when the last one has arrived. Synchronous. */
+int moshi_init_weights(moshi_ctx* ctx, const moshi_tensor* tensors, int n);
+
+/* Start conversation b afresh (b = -1: all): position 0, previous frame =
+ * the all-pad initial frame V_0 ([W] "使用 RQ-Transformer ...": fixed initial
+ * token), its KV pages returned to the pool. */
+int moshi_reset(moshi_ctx* ctx, int b);
+
+/* One frame for conversations 0..batch-1 ([W] Fig. 4 and the inference
+ * paragraph after it; [N] 3d). Each conversation at position p consumes its
+ * stored previous frame V_{s-1}, runs the Temporal Transformer one position,
+ * takes the text token, then the Depth Transformer over Moshi's 8 codebooks.
+ *   user_codes [batch][8]: the user's slots 9..16 of this frame (model order).
+ *   force [batch][9] or NULL: Moshi's slots 0..8 to use instead of the
+ *       model's own as depth inputs and as the stored frame (teacher forcing).
+ *   out_tokens [batch][9]: the model's own greedy tokens (argmax, lowest index
+ *       on ties); acoustic slots 2..8 are pad while p < delay.
+ *   out_text_logits [batch][vocab_text], out_audio_logits [batch][8][codebook]:
+ *       optional (NULL) float32 logits.
+ * Errors: MOSHI_ECONTEXT if some conversation is at ctx_max; MOSHI_EINVAL for
+ * ids outside [0, pad] (with MOSHI_DEVICE_PTRS reported by moshi_sync). */
+int moshi_step(moshi_ctx* ctx, int32_t batch, const int32_t* user_codes, const int32_t* force,
+               int32_t* out_tokens, float* out_text_logits, float* out_audio_logits, int32_t flags);
+
+/* Teacher-forced pass over tokens [B][S][17] = V_1..V_S in model order
+ * (inputs V_0..V_{S-1}, V_0 the pad frame) for conversations 0..B-1, which
+ * must be at position 0. Outputs (each optional): text_logits [B][S][vocab_text],
+ * audio_logits [B][S][8][codebook], loss. With MOSHI_TF_FILL_KV the
+ * conversations continue streaming at frame S+1; otherwise they are reset. */
+int moshi_forward_teacher_forced(moshi_ctx* ctx, const int32_t* tokens, int32_t B, int32_t S,
+                                 int32_t flags, float* text_logits, float* audio_logits,
+                                 moshi_loss* loss);
+
+/* Wait for queued work; reports device-side id errors of MOSHI_DEVICE_PTRS calls. */
+int moshi_sync(moshi_ctx* ctx);
+
+/* Current position (frames consumed) of conversation b, or a negative code. */
+int moshi_position(const moshi_ctx* ctx, int b);
+
+/* Host helper, [W] "音频建模 / 声学延迟" (eq. 4) and [N] 3c: codec frames
+ * frames[T][8] -> model order out[T][8]: out[s][0] = frames[s][0],
+ * out[s][q] = frames[s - tau][q] for q >= 1, pad where s - tau < 0. */
+int moshi_delay_codes(const int32_t* frames, int32_t T, int32_t tau, int32_t pad, int32_t* out);
+
+/* Host helper, inverse of moshi_delay_codes: model[T][8] -> out[T - tau][8]. */
+int moshi_undelay_codes(const int32_t* model, int32_t T, int32_t tau, int32_t* out);
+
+/* Last error message of ctx (or of the last failed moshi_create when ctx is NULL). */
+const char* moshi_last_error(const moshi_ctx* ctx);
+
+/* Release the context (not the caller's workspace). */
+void moshi_destroy(moshi_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSHI_H */
