@@ -1,0 +1,204 @@
+"""Benchmark of the RQ-Transformer frame step on one MI355X.
+
+Default workload: the 7B-shape bf16 model at batch 1 -- a 375-frame random
+prompt prefilled into the KV cache, then 250 greedy frames with new random user
+codes every frame. Prints one JSON line (frames/s, ms per frame, roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample).
+
+    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|mid_bf16|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def joint_prompt(fds, cfg, b, n_frames, seed=0):
+    """Random codec frames -> model-order frames [n, 17] (delay applied by the library's helper)."""
+    from synth import raw_frames
+    fr = raw_frames(cfg, b, n_frames, seed)
+    V = np.empty((n_frames, 17), np.int32)
+    V[:, 0] = fr["text"]
+    V[:, 1:9] = fds.moshi_delay_codes(fr["moshi"], cfg.delay, cfg.pad_audio)
+    V[:, 9:] = fds.moshi_delay_codes(fr["user"], cfg.delay, cfg.pad_audio)
+    return V
+
+
+def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
+    """The oracle (float32) on the host: prefill untimed, then `frames` greedy frames
+    of conversation 0 timed."""
+    from oracle import Oracle, Session
+    cores = len(os.sched_getaffinity(0))
+    m = Oracle(cfg, weights, dtype=np.float32)
+    sess = Session(m)
+    t0 = time.perf_counter()
+    if P:
+        z, _ = m.temporal(np.concatenate([m.initial_frame[None], prompts[0][:P - 1]]), 0, sess.cache)
+        sess.pos = P
+        sess.prev = prompts[0][P - 1].copy()
+    t_prefill = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(frames):
+        sess.step(users[0][P + i])
+    dt = time.perf_counter() - t0
+    return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
+            "sample": f"{frames} greedy frames of one conversation at positions {P}..{P + frames - 1} "
+                      f"(float32 NumPy oracle; prompt prefill {t_prefill:.1f} s untimed); "
+                      f"a batch of {B} costs {B}x on the host",
+            "ms_per_frame": round(dt * 1000 / frames, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="b1_7b")
+    ap.add_argument("--cpu-frames", type=int, default=None, help="oracle frames timed on the host (0: skip)")
+    ap.add_argument("--kernel-iters", type=int, default=320)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the frame step runs on a "
+              f"single MI355X; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import full_duplex_speech_amd as fds
+    from synth import config, generate_weights, param_count
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    cfg = config(args.config)
+    tf_mode = cfg.tf_frames > 0
+    B = cfg.tf_batch if tf_mode else cfg.batch
+    P = cfg.prompt_frames
+    K = args.steps if args.steps is not None else (1 if tf_mode else cfg.gen_frames)
+    W = args.warmup if not tf_mode else min(args.warmup, 1)
+    cpu_frames = args.cpu_frames if args.cpu_frames is not None else (0 if tf_mode else (50 if cfg.d_t < 1024 else 6))
+
+    t0 = time.perf_counter()
+    weights = generate_weights(cfg, seed=0)
+    log(f"weights: {param_count(cfg) / 1e9:.3f} B params generated in {time.perf_counter() - t0:.1f} s")
+    max_tf = B * cfg.tf_frames if tf_mode else 0
+    eng = fds.Moshi(cfg, max_batch=B, max_tf_tokens=max_tf)
+    t0 = time.perf_counter()
+    eng.load_weights(weights)
+    log(f"weights uploaded in {time.perf_counter() - t0:.1f} s; workspace {eng.ws_bytes / 1e9:.2f} GB")
+    ctx = eng.ctx
+
+    if tf_mode:
+        S = cfg.tf_frames
+        V = np.stack([joint_prompt(fds, cfg, b, S) for b in range(B)])
+        tok_dev = torch.from_numpy(V).cuda()
+        torch.cuda.synchronize()
+        loss = fds.moshi_loss()
+        for _ in range(W):
+            fds.moshi_forward_teacher_forced(ctx, tok_dev, B, S, fds.MOSHI_DEVICE_PTRS, None, None, loss)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            fds.moshi_forward_teacher_forced(ctx, tok_dev, B, S, fds.MOSHI_DEVICE_PTRS, None, None, loss)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        frames_per_step = B * S
+        log(f"teacher-forced: ce_text {loss.ce_text:.4f} ce_audio {loss.ce_audio:.4f}")
+        workload = {"workload": f"7B-shape teacher-forced scoring, {B} x {S} frames", "config": cfg.name,
+                    "batch": B, "frames": S}
+    else:
+        n_total = P + K + W
+        prompts = [joint_prompt(fds, cfg, b, n_total) for b in range(B)]
+        users = [p[:, 9:] for p in prompts]
+        user_dev = torch.from_numpy(np.stack([users[b][P:P + max(K, W)] for b in range(B)], axis=1).copy()).cuda()
+        out_dev = torch.empty((max(K, W), B, 9), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+
+        def prefill():
+            eng.reset()
+            if P:
+                pr = np.ascontiguousarray(np.stack([p[:P] for p in prompts]))
+                fds.moshi_forward_teacher_forced(ctx, pr, B, P, fds.MOSHI_TF_FILL_KV | fds.MOSHI_TF_SKIP_DEPTH)
+
+        t0 = time.perf_counter()
+        prefill()
+        log(f"prefill {B} x {P} frames in {time.perf_counter() - t0:.2f} s")
+        for i in range(W):
+            fds.moshi_step(ctx, B, user_dev[i], None, out_dev[i], None, None, fds.MOSHI_DEVICE_PTRS)
+        fds.moshi_sync(ctx)
+        prefill()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fds.moshi_step(ctx, B, user_dev[i], None, out_dev[i], None, None, fds.MOSHI_DEVICE_PTRS)
+        fds.moshi_sync(ctx)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        frames_per_step = B
+        log(f"{K} steps of {B} frame(s): {dt * 1000 / K:.3f} ms/step; last tokens {out_dev[K - 1, 0].tolist()}")
+        workload = {"workload": f"7B-shape streaming decode, batch {B}, {P}-frame prompt then {K} greedy frames"
+                    if cfg.d_t == 4096 else f"{cfg.name} streaming decode, batch {B}, {P}-frame prompt then "
+                    f"{K} greedy frames", "config": cfg.name, "batch": B, "prompt_frames": P, "frames": K}
+
+    ms_per_step = dt * 1000 / K
+    value = frames_per_step * K / dt
+
+    # dominant kernel: the SwiGLU gate/up weight stream (the largest share of the frame's bytes)
+    roofline = None
+    if not tf_mode:
+        us, nbytes = fds.moshi_time_kernel(ctx, "ffn_gate_up", B, args.kernel_iters)
+        ach = nbytes / (us * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "k_gemv (RMSNorm + gate/up + SiLU product, one temporal layer)",
+                    "bytes_per_launch": nbytes, "us_per_launch": round(us, 3)}
+        others = {}
+        for kname in ("qkv", "wo", "ffn_down", "text_head", "attn"):
+            kus, kb = fds.moshi_time_kernel(ctx, kname, B, 64)
+            others[kname] = {"us": round(kus, 2), "GB/s": round(kb / (kus * 1e-6) / 1e9, 1)}
+        roofline["other_kernels"] = others
+        # whole-frame algorithmic bytes: every weight once + K/V read at the mean context
+        esz = 2 if cfg.dtype == "bf16" else 4
+        lin = param_count(cfg) - (cfg.vocab_text + 1 + 16 * (cfg.codebook + 1)) * cfg.d_t \
+            - (cfg.vocab_text + 1 + 7 * (cfg.codebook + 1)) * cfg.d_d
+        mean_ctx = P + (K + 1) / 2
+        kv = B * cfg.n_layers_t * 2 * cfg.d_t * esz * mean_ctx
+        frame_bytes = lin * esz + kv
+        roofline["frame_bytes_per_step"] = frame_bytes
+        roofline["frame_frac"] = round(frame_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    cpu = None
+    if cpu_frames:
+        log(f"cpu baseline: oracle float32, {cpu_frames} frames")
+        cpu = cpu_baseline(cfg, weights, B, P, cpu_frames, prompts, users)
+
+    out = {
+        "metric": "RQ-Transformer frames/sec and ms/frame at batch 1 and 8 (7B shape, bf16)",
+        "value": round(value, 3), "unit": "frames/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-init weights, uniform random tokens)",
+        "config": workload, "roofline": roofline, "cpu_baseline": cpu,
+        "host": {"cpu": platform.processor() or platform.machine(), "cores": len(os.sched_getaffinity(0))},
+    }
+    print(json.dumps(out), flush=True)
+    eng.close()
+
+
+if __name__ == "__main__":
+    main()

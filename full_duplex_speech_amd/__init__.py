@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     moshi_reset,
     moshi_step,
     moshi_sync,
+    moshi_time_kernel,
     moshi_undelay_codes,
     moshi_workspace_bytes,
 )

@@ -56,8 +56,9 @@ class moshi_loss(ctypes.Structure):
 EXPORTS = (
     "moshi_workspace_bytes", "moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset",
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
-    "moshi_undelay_codes", "moshi_last_error", "moshi_destroy",
+    "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel",
 )
+KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5}
 
 _lib = None
 
@@ -85,11 +86,12 @@ def lib() -> ctypes.CDLL:
     L.moshi_undelay_codes.argtypes = [VP, I32, I32, VP]
     L.moshi_last_error.argtypes = [VP]
     L.moshi_last_error.restype = ctypes.c_char_p
+    L.moshi_time_kernel.argtypes = [VP, I32, I32, I32, P(ctypes.c_float), P(ctypes.c_double)]
     L.moshi_destroy.argtypes = [VP]
     L.moshi_destroy.restype = None
     for n in ("moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset", "moshi_step",
               "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
-              "moshi_undelay_codes"):
+              "moshi_undelay_codes", "moshi_time_kernel"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -206,6 +208,14 @@ def moshi_undelay_codes(model: np.ndarray, tau: int) -> np.ndarray:
     out = np.empty((max(m.shape[0] - tau, 0), 8), dtype=np.int32)
     _check(None, lib().moshi_undelay_codes(_ptr(m), m.shape[0], tau, _ptr(out) if out.size else None))
     return out
+
+
+def moshi_time_kernel(ctx, kernel: str, batch: int, iters: int) -> Tuple[float, float]:
+    """(mean microseconds per launch, algorithmic bytes per launch) of one frame kernel."""
+    us = ctypes.c_float()
+    nbytes = ctypes.c_double()
+    _check(ctx, lib().moshi_time_kernel(ctx, KERNELS[kernel], batch, iters, ctypes.byref(us), ctypes.byref(nbytes)))
+    return float(us.value), float(nbytes.value)
 
 
 def moshi_last_error(ctx) -> str:

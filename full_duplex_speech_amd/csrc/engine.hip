@@ -329,16 +329,149 @@ KvView depth_kv(moshi_ctx* c) {
   return v;
 }
 
+// Argument builders of the frame's kernels (shared by the frame sequence and
+// the kernel timer).
+GemvArgs qkv_args(moshi_ctx* c, const LayerW& w, int layer, bool depth_model, int pos_const) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int D = depth_model ? g.d_d : g.d_t;
+  GemvArgs a{};
+  a.eps = g.norm_eps;
+  a.W = c->ws + w.wqkv;
+  a.N = 3 * D;
+  a.K = D;
+  a.x = c->at<float>(depth_model ? p.hd : p.h);
+  a.ldx = D;
+  a.gain = c->at<float>(w.attn_norm);
+  a.y = c->at<float>(depth_model ? p.dq : p.q);
+  a.ldy = D;
+  a.pos = depth_model ? nullptr : c->at<int>(p.st_pos);
+  a.pos_const = pos_const;
+  a.rope = c->at<float>(depth_model ? p.rope_d : p.rope_t);
+  a.hd = D / (depth_model ? g.n_heads_d : g.n_heads_t);
+  a.d = D;
+  a.kv = depth_model ? depth_kv(c) : temporal_kv(c);
+  a.kv_bf16 = depth_model ? 0 : p.bf;
+  a.layer = layer;
+  return a;
+}
+
+AttnArgs attn_args(moshi_ctx* c, int layer, bool depth_model, int pos_const) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int D = depth_model ? g.d_d : g.d_t;
+  const int hd = D / (depth_model ? g.n_heads_d : g.n_heads_t);
+  AttnArgs at{};
+  at.q = c->at<float>(depth_model ? p.dq : p.q);
+  at.ldq = D;
+  at.kv = depth_model ? depth_kv(c) : temporal_kv(c);
+  at.layer = layer;
+  at.pos = depth_model ? nullptr : c->at<int>(p.st_pos);
+  at.pos_const = pos_const;
+  at.split = depth_model ? g.n_q : g.page_frames;
+  at.part = c->at<float>(depth_model ? p.part_d : p.part_t);
+  at.max_splits = depth_model ? 1 : p.max_splits;
+  at.counters = c->at<int>(depth_model ? p.st_cnt_d : p.st_cnt_t);
+  at.out = c->at<float>(depth_model ? p.dattn : p.attn);
+  at.ldo = D;
+  at.scale = 1.0f / sqrtf((float)hd);
+  return at;
+}
+
+GemvArgs wo_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
+  const Plan& p = c->plan;
+  const int D = depth_model ? c->cfg.d_d : c->cfg.d_t;
+  GemvArgs o{};
+  o.W = c->ws + w.wo;
+  o.N = D;
+  o.K = D;
+  o.x = c->at<float>(depth_model ? p.dattn : p.attn);
+  o.ldx = D;
+  o.y = c->at<float>(depth_model ? p.hd : p.h);
+  o.ldy = D;
+  return o;
+}
+
+GemvArgs gu_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int D = depth_model ? g.d_d : g.d_t, F = depth_model ? g.ffn_d : g.ffn_t;
+  GemvArgs f{};
+  f.eps = g.norm_eps;
+  f.W = c->ws + w.wgu;
+  f.N = 2 * F;
+  f.K = D;
+  f.x = c->at<float>(depth_model ? p.hd : p.h);
+  f.ldx = D;
+  f.gain = c->at<float>(w.ffn_norm);
+  f.y = c->at<float>(depth_model ? p.dinter : p.inter);
+  f.ldy = F;
+  return f;
+}
+
+GemvArgs down_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  const int D = depth_model ? g.d_d : g.d_t, F = depth_model ? g.ffn_d : g.ffn_t;
+  GemvArgs dn{};
+  dn.W = c->ws + w.wdown;
+  dn.N = D;
+  dn.K = F;
+  dn.x = c->at<float>(depth_model ? p.dinter : p.inter);
+  dn.ldx = F;
+  dn.y = c->at<float>(depth_model ? p.hd : p.h);
+  dn.ldy = D;
+  return dn;
+}
+
+GemvArgs text_head_args(moshi_ctx* c) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  GemvArgs a{};
+  a.eps = g.norm_eps;
+  a.W = c->ws + p.text_head;
+  a.N = g.vocab_text;
+  a.K = g.d_t;
+  a.x = c->at<float>(p.h);
+  a.ldx = g.d_t;
+  a.gain = c->at<float>(p.out_norm);
+  a.y = c->at<float>(p.text_logits);
+  a.ldy = g.vocab_text;
+  return a;
+}
+
+ArgmaxArgs argmax_args(moshi_ctx* c, int slot) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  ArgmaxArgs m{};
+  if (slot == 0) {
+    m.logits = c->at<float>(p.text_logits);
+    m.n = g.vocab_text;
+    m.ld = g.vocab_text;
+  } else {
+    m.logits = c->at<float>(p.audio_logits) + (long long)(slot - 1) * g.codebook;
+    m.n = g.codebook;
+    m.ld = g.n_q * g.codebook;
+  }
+  m.slot = slot;
+  m.pad_after = slot >= 2;
+  m.pad_id = g.codebook;
+  m.delay = g.delay;
+  m.pos = c->at<int>(p.st_pos);
+  m.out_tok = c->at<int>(p.st_out_tok);
+  m.cur_tok = c->at<int>(p.st_cur_tok);
+  m.force = c->at<int>(p.st_force);
+  m.has_force = c->at<int>(p.st_has_force);
+  return m;
+}
+
 // Enqueue one frame for conversations 0..B-1 (no host interaction).
 void enqueue_step(moshi_ctx* c, int B, bool depth) {
   const moshi_config& g = c->cfg;
   const Plan& p = c->plan;
   hipStream_t s = c->stream;
   const bool bf = p.bf;
-  const int d = g.d_t, F = g.ffn_t, dd = g.d_d, Fd = g.ffn_d;
-  const int hdt = d / g.n_heads_t, hdd = dd / g.n_heads_d;
-  int* pos = c->at<int>(p.st_pos);
-  int* cur = c->at<int>(p.st_cur_tok);
+  const int hdt = g.d_t / g.n_heads_t, hdd = g.d_d / g.n_heads_d;
 
   EmbedArgs ea{};
   ea.table = c->ws + p.emb_t;
@@ -346,227 +479,70 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   ea.rows = c->at<int>(p.meta_rows);
   ea.frames = c->at<int>(p.st_prev);
   ea.h = c->at<float>(p.h);
-  ea.d = d;
+  ea.d = g.d_t;
   ea.err = c->at<int>(p.st_err);
   launch_embed(ea, B, bf, s);
 
-  const KvView tkv = temporal_kv(c);
   for (int l = 0; l < g.n_layers_t; ++l) {
     const LayerW& w = p.lt[l];
-    GemvArgs a{};
-    a.eps = g.norm_eps;
-    // RMSNorm -> Wq|Wk|Wv -> RoPE -> q, KV append
-    a.W = c->ws + w.wqkv;
-    a.N = 3 * d;
-    a.K = d;
-    a.x = c->at<float>(p.h);
-    a.ldx = d;
-    a.gain = c->at<float>(w.attn_norm);
-    a.y = c->at<float>(p.q);
-    a.ldy = d;
-    a.pos = pos;
-    a.rope = c->at<float>(p.rope_t);
-    a.hd = hdt;
-    a.d = d;
-    a.kv = tkv;
-    a.kv_bf16 = bf;
-    a.layer = l;
-    launch_gemv(a, B, EPI_QKV, bf, s);
-    // attention over positions 0..pos
-    AttnArgs at{};
-    at.q = c->at<float>(p.q);
-    at.ldq = d;
-    at.kv = tkv;
-    at.layer = l;
-    at.pos = pos;
-    at.split = g.page_frames;
-    at.part = c->at<float>(p.part_t);
-    at.max_splits = p.max_splits;
-    at.counters = c->at<int>(p.st_cnt_t);
-    at.out = c->at<float>(p.attn);
-    at.ldo = d;
-    at.scale = 1.0f / sqrtf((float)hdt);
-    launch_attn_decode(at, B, g.n_heads_t, hdt, bf, s);
-    // h += Wo attn
-    GemvArgs o{};
-    o.W = c->ws + w.wo;
-    o.N = d;
-    o.K = d;
-    o.x = c->at<float>(p.attn);
-    o.ldx = d;
-    o.y = c->at<float>(p.h);
-    o.ldy = d;
-    launch_gemv(o, B, EPI_RESID, bf, s);
-    // SwiGLU: inter = SiLU(Wg n) * (Wu n), n = RMSNorm(h)
-    GemvArgs f{};
-    f.eps = g.norm_eps;
-    f.W = c->ws + w.wgu;
-    f.N = 2 * F;
-    f.K = d;
-    f.x = c->at<float>(p.h);
-    f.ldx = d;
-    f.gain = c->at<float>(w.ffn_norm);
-    f.y = c->at<float>(p.inter);
-    f.ldy = F;
-    launch_gemv(f, B, EPI_SWIGLU, bf, s);
-    // h += Wdown inter
-    GemvArgs dn{};
-    dn.W = c->ws + w.wdown;
-    dn.N = d;
-    dn.K = F;
-    dn.x = c->at<float>(p.inter);
-    dn.ldx = F;
-    dn.y = c->at<float>(p.h);
-    dn.ldy = d;
-    launch_gemv(dn, B, EPI_RESID, bf, s);
+    launch_gemv(qkv_args(c, w, l, false, 0), B, EPI_QKV, bf, s);    // RMSNorm, Wqkv, RoPE, KV append
+    launch_attn_decode(attn_args(c, l, false, 0), B, g.n_heads_t, hdt, bf, s);  // keys 0..pos
+    launch_gemv(wo_args(c, w, false), B, EPI_RESID, bf, s);         // h += Wo attn
+    launch_gemv(gu_args(c, w, false), B, EPI_SWIGLU, bf, s);        // SiLU(Wg n) * Wu n
+    launch_gemv(down_args(c, w, false), B, EPI_RESID, bf, s);       // h += Wdown inter
   }
   // text head on z = RMSNorm(h), greedy text token
-  {
-    GemvArgs a{};
-    a.eps = g.norm_eps;
-    a.W = c->ws + p.text_head;
-    a.N = g.vocab_text;
-    a.K = d;
-    a.x = c->at<float>(p.h);
-    a.ldx = d;
-    a.gain = c->at<float>(p.out_norm);
-    a.y = c->at<float>(p.text_logits);
-    a.ldy = g.vocab_text;
-    launch_gemv(a, B, EPI_STORE, bf, s);
-    ArgmaxArgs m{};
-    m.logits = c->at<float>(p.text_logits);
-    m.n = g.vocab_text;
-    m.ld = g.vocab_text;
-    m.slot = 0;
-    m.pad_after = 0;
-    m.pos = pos;
-    m.out_tok = c->at<int>(p.st_out_tok);
-    m.cur_tok = cur;
-    m.force = c->at<int>(p.st_force);
-    m.has_force = c->at<int>(p.st_has_force);
-    launch_argmax(m, B, s);
-  }
+  launch_gemv(text_head_args(c), B, EPI_STORE, bf, s);
+  launch_argmax(argmax_args(c, 0), B, s);
   if (depth) {
-    const KvView dkv = depth_kv(c);
     for (int j = 0; j < g.n_q; ++j) {
       const DepthW& w = p.dj[j];
       // u_j = W_in^j z + E_D^j[token of slot j]
       GemvArgs a{};
       a.eps = g.norm_eps;
       a.W = c->ws + w.in_proj;
-      a.N = dd;
-      a.K = d;
+      a.N = g.d_d;
+      a.K = g.d_t;
       a.x = c->at<float>(p.h);
-      a.ldx = d;
+      a.ldx = g.d_t;
       a.gain = c->at<float>(p.out_norm);
       a.y = c->at<float>(p.hd);
-      a.ldy = dd;
+      a.ldy = g.d_d;
       a.emb = c->ws + w.emb;
-      a.tok = cur;
+      a.tok = c->at<int>(p.st_cur_tok);
       a.tok_stride = kSlots;
       a.tok_col = j;
       a.tok_rows = (j == 0 ? g.vocab_text : g.codebook) + 1;
       launch_gemv(a, B, EPI_EMB, bf, s);
       for (int l = 0; l < g.n_layers_d; ++l) {
         const LayerW& lw = w.layers[l];
-        GemvArgs q{};
-        q.eps = g.norm_eps;
-        q.W = c->ws + lw.wqkv;
-        q.N = 3 * dd;
-        q.K = dd;
-        q.x = c->at<float>(p.hd);
-        q.ldx = dd;
-        q.gain = c->at<float>(lw.attn_norm);
-        q.y = c->at<float>(p.dq);
-        q.ldy = dd;
-        q.pos = nullptr;
-        q.pos_const = j;
-        q.rope = c->at<float>(p.rope_d);
-        q.hd = hdd;
-        q.d = dd;
-        q.kv = dkv;
-        q.kv_bf16 = 0;
-        q.layer = l;
-        launch_gemv(q, B, EPI_QKV, bf, s);
-        AttnArgs at{};
-        at.q = c->at<float>(p.dq);
-        at.ldq = dd;
-        at.kv = dkv;
-        at.layer = l;
-        at.pos = nullptr;
-        at.pos_const = j;
-        at.split = g.n_q;
-        at.part = c->at<float>(p.part_d);
-        at.max_splits = 1;
-        at.counters = c->at<int>(p.st_cnt_d);
-        at.out = c->at<float>(p.dattn);
-        at.ldo = dd;
-        at.scale = 1.0f / sqrtf((float)hdd);
-        launch_attn_decode(at, B, g.n_heads_d, hdd, false, s);
-        GemvArgs o{};
-        o.W = c->ws + lw.wo;
-        o.N = dd;
-        o.K = dd;
-        o.x = c->at<float>(p.dattn);
-        o.ldx = dd;
-        o.y = c->at<float>(p.hd);
-        o.ldy = dd;
-        launch_gemv(o, B, EPI_RESID, bf, s);
-        GemvArgs f{};
-        f.eps = g.norm_eps;
-        f.W = c->ws + lw.wgu;
-        f.N = 2 * Fd;
-        f.K = dd;
-        f.x = c->at<float>(p.hd);
-        f.ldx = dd;
-        f.gain = c->at<float>(lw.ffn_norm);
-        f.y = c->at<float>(p.dinter);
-        f.ldy = Fd;
-        launch_gemv(f, B, EPI_SWIGLU, bf, s);
-        GemvArgs dn{};
-        dn.W = c->ws + lw.wdown;
-        dn.N = dd;
-        dn.K = Fd;
-        dn.x = c->at<float>(p.dinter);
-        dn.ldx = Fd;
-        dn.y = c->at<float>(p.hd);
-        dn.ldy = dd;
-        launch_gemv(dn, B, EPI_RESID, bf, s);
+        launch_gemv(qkv_args(c, lw, l, true, j), B, EPI_QKV, bf, s);
+        launch_attn_decode(attn_args(c, l, true, j), B, g.n_heads_d, hdd, false, s);
+        launch_gemv(wo_args(c, lw, true), B, EPI_RESID, bf, s);
+        launch_gemv(gu_args(c, lw, true), B, EPI_SWIGLU, bf, s);
+        launch_gemv(down_args(c, lw, true), B, EPI_RESID, bf, s);
       }
       GemvArgs hh{};
       hh.eps = g.norm_eps;
       hh.W = c->ws + w.head;
       hh.N = g.codebook;
-      hh.K = dd;
+      hh.K = g.d_d;
       hh.x = c->at<float>(p.hd);
-      hh.ldx = dd;
+      hh.ldx = g.d_d;
       hh.gain = c->at<float>(w.out_norm);
       hh.y = c->at<float>(p.audio_logits) + (long long)j * g.codebook;
       hh.ldy = g.n_q * g.codebook;
       launch_gemv(hh, B, EPI_STORE, bf, s);
-      ArgmaxArgs m{};
-      m.logits = c->at<float>(p.audio_logits) + (long long)j * g.codebook;
-      m.n = g.codebook;
-      m.ld = g.n_q * g.codebook;
-      m.slot = j + 1;
-      m.pad_after = j >= 1;
-      m.pad_id = g.codebook;
-      m.delay = g.delay;
-      m.pos = pos;
-      m.out_tok = c->at<int>(p.st_out_tok);
-      m.cur_tok = cur;
-      m.force = c->at<int>(p.st_force);
-      m.has_force = c->at<int>(p.st_has_force);
-      launch_argmax(m, B, s);
+      launch_argmax(argmax_args(c, j + 1), B, s);
     }
   }
   AdvanceArgs av{};
-  av.cur_tok = cur;
+  av.cur_tok = c->at<int>(p.st_cur_tok);
   av.force = c->at<int>(p.st_force);
   av.has_force = c->at<int>(p.st_has_force);
   av.user = c->at<int>(p.st_user);
   av.prev = c->at<int>(p.st_prev);
-  av.pos = pos;
+  av.pos = c->at<int>(p.st_pos);
   av.err = c->at<int>(p.st_err);
   av.pad_text = g.vocab_text;
   av.pad_audio = g.codebook;
@@ -924,6 +900,90 @@ int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B,
     if (!(flags & MOSHI_TF_FILL_KV))
       for (int b = 0; b < B; ++b) reset_conv(c, b);
     order_out(c);
+  });
+}
+
+int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters, float* avg_us,
+                      double* bytes_per_launch) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    const moshi_config& g = c->cfg;
+    const Plan& p = c->plan;
+    if (!c->ready) fail(MOSHI_ESTATE, "weights not loaded");
+    if (batch < 1 || batch > g.max_batch) fail(MOSHI_EINVAL, "batch %d out of range", batch);
+    if (iters < 1 || !avg_us || !bytes_per_launch) fail(MOSHI_EINVAL, "bad iters or output pointers");
+    if (kernel < 0 || kernel > MOSHI_KERNEL_ATTN) fail(MOSHI_EINVAL, "unknown kernel id %d", kernel);
+    const double e = p.esz;
+    const double d = g.d_t, F = g.ffn_t, B = batch;
+    for (int b = 0; b < batch; ++b)
+      if (kernel == MOSHI_KERNEL_ATTN && c->pos_h[b] < 1) fail(MOSHI_ESTATE, "attention timing needs a filled cache");
+    double bytes = 0;
+    auto enqueue = [&](int l) {
+      const LayerW& w = p.lt[l];
+      switch (kernel) {
+        case MOSHI_KERNEL_QKV: {
+          // time the projection only: the KV append writes into the page of the
+          // next free position, which the next step overwrites anyway
+          GemvArgs a = qkv_args(c, w, l, false, 0);
+          launch_gemv(a, batch, EPI_QKV, p.bf, c->stream);
+          bytes = 3 * d * d * e + B * (d * 4 + d * 4 + 2 * d * e);
+          break;
+        }
+        case MOSHI_KERNEL_WO:
+          launch_gemv(wo_args(c, w, false), batch, EPI_RESID, p.bf, c->stream);
+          bytes = d * d * e + B * 3 * d * 4;
+          break;
+        case MOSHI_KERNEL_FFN_GATE_UP:
+          launch_gemv(gu_args(c, w, false), batch, EPI_SWIGLU, p.bf, c->stream);
+          bytes = 2 * F * d * e + B * (d + F) * 4;
+          break;
+        case MOSHI_KERNEL_FFN_DOWN:
+          launch_gemv(down_args(c, w, false), batch, EPI_RESID, p.bf, c->stream);
+          bytes = d * F * e + B * (F + 2 * d) * 4;
+          break;
+        case MOSHI_KERNEL_TEXT_HEAD:
+          launch_gemv(text_head_args(c), batch, EPI_STORE, p.bf, c->stream);
+          bytes = g.vocab_text * d * e + B * (d + g.vocab_text) * 4;
+          break;
+        case MOSHI_KERNEL_ATTN: {
+          // keys 0..pos-1 of the filled cache: read K and V once
+          launch_attn_decode(attn_args(c, l, false, 0), batch, g.n_heads_t, g.d_t / g.n_heads_t, p.bf, c->stream);
+          double keys = 0;
+          for (int b = 0; b < batch; ++b) keys += c->pos_h[b] + 1;
+          bytes = keys * 2 * d * (p.bf ? 2 : 4) + B * 2 * d * 4;
+          break;
+        }
+      }
+    };
+    if (kernel == MOSHI_KERNEL_QKV)
+      for (int b = 0; b < batch; ++b) ensure_pages(c, b, c->pos_h[b] + 1);  // the append stays in own pages
+    hipEvent_t e0, e1;
+    HIPCHECK(hipEventCreate(&e0));
+    HIPCHECK(hipEventCreate(&e1));
+    // the attention reads positions 0..pos[b]; pos is the next position, whose
+    // key slot holds whatever the last step wrote there: stay inside the cache
+    // by stepping the device position back by one for the timing
+    if (kernel == MOSHI_KERNEL_ATTN) {
+      for (int b = 0; b < batch; ++b) c->pin_in[b] = c->pos_h[b] - 1;
+      HIPCHECK(hipMemcpyAsync(c->ws + p.st_pos, c->pin_in, batch * 4, hipMemcpyHostToDevice, c->stream));
+    }
+    for (int i = 0; i < g.n_layers_t; ++i) enqueue(i);  // warm
+    HIPCHECK(hipEventRecord(e0, c->stream));
+    for (int i = 0; i < iters; ++i) enqueue(i % g.n_layers_t);
+    HIPCHECK(hipEventRecord(e1, c->stream));
+    HIPCHECK(hipEventSynchronize(e1));
+    float ms = 0;
+    HIPCHECK(hipEventElapsedTime(&ms, e0, e1));
+    if (kernel == MOSHI_KERNEL_ATTN) {
+      for (int b = 0; b < batch; ++b) c->pin_in[b] = c->pos_h[b];
+      HIPCHECK(hipMemcpyAsync(c->ws + p.st_pos, c->pin_in, batch * 4, hipMemcpyHostToDevice, c->stream));
+      HIPCHECK(hipStreamSynchronize(c->stream));
+    }
+    HIPCHECK(hipEventDestroy(e0));
+    HIPCHECK(hipEventDestroy(e1));
+    HIPCHECK(hipGetLastError());
+    *avg_us = ms * 1000.f / iters;
+    *bytes_per_launch = bytes;
   });
 }
 

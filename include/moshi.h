@@ -157,6 +157,24 @@ int moshi_forward_teacher_forced(moshi_ctx* ctx, const int32_t* tokens, int32_t 
                                  int32_t flags, float* text_logits, float* audio_logits,
                                  moshi_loss* loss);
 
+/* Kernels that moshi_time_kernel can time. */
+#define MOSHI_KERNEL_QKV 0        /* RMSNorm + Wq|Wk|Wv + RoPE + KV append, one temporal layer */
+#define MOSHI_KERNEL_WO 1         /* output projection + residual, one temporal layer */
+#define MOSHI_KERNEL_FFN_GATE_UP 2 /* RMSNorm + gate/up + SiLU product, one temporal layer */
+#define MOSHI_KERNEL_FFN_DOWN 3   /* down projection + residual, one temporal layer */
+#define MOSHI_KERNEL_TEXT_HEAD 4  /* final RMSNorm + text head */
+#define MOSHI_KERNEL_ATTN 5       /* causal decode attention over the filled cache, one layer */
+
+/* Measurement: launch one kernel of the frame `iters` times on the context
+ * stream, cycling over the temporal layers' weights (so that weights come from
+ * HBM as in a real frame), between two HIP events; returns the mean time per
+ * launch in microseconds and the algorithmic bytes one launch must move
+ * (weights, plus activations, plus K/V for attention). Uses the current
+ * activations and, for attention, the filled KV cache (position >= 1). The
+ * conversation state is left unchanged except for scratch activations. */
+int moshi_time_kernel(moshi_ctx* ctx, int32_t kernel, int32_t batch, int32_t iters, float* avg_us,
+                      double* bytes_per_launch);
+
 /* Wait for queued work; reports device-side id errors of MOSHI_DEVICE_PTRS calls. */
 int moshi_sync(moshi_ctx* ctx);
 
