@@ -176,7 +176,8 @@ Plan make_plan(const moshi_config& c) {
   p.page_table = p.take((size_t)c.max_batch * p.max_pages_conv * 4);
   p.depth_kv_elems = (long long)c.n_layers_d * 2 * c.d_d * c.n_q;
   p.depth_kv = p.take((size_t)c.max_batch * p.depth_kv_elems * 4);
-  p.max_splits = p.max_pages_conv;
+  // attention splits: every split covers at most 512 keys at full context
+  p.max_splits = (c.ctx_max + 511) / 512;
   // state
   const int mb = c.max_batch;
   p.st_pos = p.take(mb * 4);
@@ -370,7 +371,7 @@ AttnArgs attn_args(moshi_ctx* c, int layer, bool depth_model, int pos_const) {
   at.pos_const = pos_const;
   at.split = depth_model ? g.n_q : g.page_frames;
   at.part = c->at<float>(depth_model ? p.part_d : p.part_t);
-  at.max_splits = depth_model ? 1 : p.max_splits;
+  at.max_splits = depth_model ? 1 : p.max_splits;  // number of key-range splits
   at.counters = c->at<int>(depth_model ? p.st_cnt_d : p.st_cnt_t);
   at.out = c->at<float>(depth_model ? p.dattn : p.attn);
   at.ldo = D;

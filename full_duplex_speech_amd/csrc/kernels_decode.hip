@@ -79,6 +79,70 @@ constexpr int kGemvRowsPerWave = 4;
 constexpr int kGemvRows = 4 * kGemvRowsPerWave;
 constexpr int kGemvLdsFloats = 16384;
 
+template <int NB, bool BF, int EPI, int RPW>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, int row0, int nrows, const float (&acc)[RPW][NB]) {
+  const int N = a.N;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float* y = a.y + (long long)b * a.ldy;
+    if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const int row = row0 + r;
+        if (row >= N) break;
+        float s = acc[r][b];
+        if (EPI == EPI_RESID) s += y[row];
+        if (EPI == EPI_EMB) {
+          const int t = min(max(a.tok[b * a.tok_stride + a.tok_col], 0), a.tok_rows - 1);
+          s += load_w1(a.emb, (long long)t * N + row, BF);
+        }
+        y[row] = s;
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // rows (2i, 2i+1) = (gate_i, up_i)
+#pragma unroll
+      for (int r = 0; r < RPW; r += 2) {
+        const int row = row0 + r;
+        if (row + 1 >= N) break;
+        const float g = acc[r][b], u = acc[r + 1][b];
+        y[row >> 1] = g / (1.0f + expf(-g)) * u;
+      }
+    } else if constexpr (EPI == EPI_QKV) {
+      const int p = a.pos ? a.pos[b] : a.pos_const;
+#pragma unroll
+      for (int r = 0; r < RPW; r += 2) {
+        const int row = row0 + r;
+        if (row + 1 >= N) break;
+        float x0 = acc[r][b], x1 = acc[r + 1][b];
+        const int part = row / a.d;  // 0 q, 1 k, 2 v
+        const int rr = row - part * a.d;
+        const int head = rr / a.hd, dim = rr - head * a.hd;
+        if (part < 2) {
+          const float* cs = a.rope + ((long long)p * (a.hd >> 1) + (dim >> 1)) * 2;
+          const float c = cs[0], sn = cs[1];
+          const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+          x0 = y0; x1 = y1;
+        }
+        if (part == 0) {
+          y[rr] = x0;
+          y[rr + 1] = x1;
+        } else {
+          const long long off = a.kv.offset(b, a.layer, part - 1, head, p) + dim;
+          if (a.kv_bf16) {
+            uint16_t* kv = (uint16_t*)a.kv.base;
+            kv[off] = f2bf(x0);
+            kv[off + 1] = f2bf(x1);
+          } else {
+            float* kv = (float*)a.kv.base;
+            kv[off] = x0;
+            kv[off + 1] = x1;
+          }
+        }
+      }
+    }
+  }
+}
+
 template <int NB, bool BF, int EPI>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a, int KC) {
   constexpr int EPL = WLoad<BF>::EPL;
@@ -168,69 +232,167 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a, int KC) {
     for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
   if (lane != 0) return;
 
+  gemv_epilogue<NB, BF, EPI, RPW>(a, row0, RPW, acc);
+}
+
+// Streaming variant used whenever the NB normalised input vectors fit in LDS
+// (NB * K * 4 bytes <= 64 KB). Each wave owns one pair of output rows and walks
+// K in groups of 8 wave-wide 16-byte loads per row; the loads of the next group
+// are in flight while the current group is multiplied, and the first group is
+// requested before the block's RMSNorm prologue so that HBM latency overlaps
+// the prologue. One row pair per wave and many resident waves (8 per block)
+// give the memory system the whole matrix's worth of requests at once.
+constexpr int kStreamWaves = 8;
+
+template <int NB, bool BF>
+struct Unit {
+  static constexpr int EPL = WLoad<BF>::EPL;
+  static constexpr int SPAN = 64 * EPL;   // elements covered by one wave-wide load
+  static constexpr int LPG = 8;           // loads per row per group
+  static constexpr int GROUP = SPAN * LPG;
+};
+
+template <bool BF>
+__device__ __forceinline__ void unpack16(const u32x4& v, float (&w)[WLoad<BF>::EPL]) {
+  if constexpr (BF) {
+    w[0] = bf_lo(v.x); w[1] = bf_hi(v.x); w[2] = bf_lo(v.y); w[3] = bf_hi(v.y);
+    w[4] = bf_lo(v.z); w[5] = bf_hi(v.z); w[6] = bf_lo(v.w); w[7] = bf_hi(v.w);
+  } else {
+    w[0] = __uint_as_float(v.x); w[1] = __uint_as_float(v.y); w[2] = __uint_as_float(v.z); w[3] = __uint_as_float(v.w);
+  }
+}
+
+template <int NB, bool BF, int EPI>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_stream(GemvArgs a) {
+  using U = Unit<NB, BF>;
+  constexpr int EPL = U::EPL, SPAN = U::SPAN, LPG = U::LPG, GROUP = U::GROUP;
+  extern __shared__ float xs[];  // [NB][K]
+  __shared__ float s_red[kStreamWaves][NB];
+  __shared__ float s_rstd[NB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+  const int row0 = (blockIdx.x * kStreamWaves + wave) * 2;
+  const int ng = (K + GROUP - 1) / GROUP;
+  const bool live = row0 < N;
+  const bool has1 = row0 + 1 < N;
+  const char* W0 = (const char*)a.W + (long long)row0 * K * (BF ? 2 : 4);
+  const char* W1 = W0 + (long long)K * (BF ? 2 : 4);
+
+  u32x4 wa[2][LPG], wb[2][LPG];
+  auto load = [&](int g, u32x4 (&w)[2][LPG]) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    float* y = a.y + (long long)b * a.ldy;
-    if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
+    for (int i = 0; i < LPG; ++i) {
+      const int k = g * GROUP + i * SPAN + lane * EPL;
+      const bool ok = k < K;
+      const long long off = (long long)k * (BF ? 2 : 4);
+      w[0][i] = (live && ok) ? __builtin_nontemporal_load((const u32x4*)(W0 + off)) : u32x4{0, 0, 0, 0};
+      w[1][i] = (has1 && ok) ? __builtin_nontemporal_load((const u32x4*)(W1 + off)) : u32x4{0, 0, 0, 0};
+    }
+  };
+  load(0, wa);
+
+  // prologue: RMSNorm statistics and the normalised inputs in LDS
+  float rs[NB];
+  if (a.gain) {
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const int row = row0 + r;
-        if (row >= N) break;
-        float s = acc[r][b];
-        if (EPI == EPI_RESID) s += y[row];
-        if (EPI == EPI_EMB) {
-          const int t = min(max(a.tok[b * a.tok_stride + a.tok_col], 0), a.tok_rows - 1);
-          s += load_w1(a.emb, (long long)t * N + row, BF);
-        }
-        y[row] = s;
+    for (int b = 0; b < NB; ++b) rs[b] = 0.f;
+    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 v = *(const float4*)(a.x + (long long)b * a.ldx + k);
+        rs[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
       }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      // rows (2i, 2i+1) = (gate_i, up_i)
+    }
 #pragma unroll
-      for (int r = 0; r < RPW; r += 2) {
-        const int row = row0 + r;
-        if (row + 1 >= N) break;
-        const float g = acc[r][b], u = acc[r + 1][b];
-        y[row >> 1] = g / (1.0f + expf(-g)) * u;
-      }
-    } else if constexpr (EPI == EPI_QKV) {
-      const int p = a.pos ? a.pos[b] : a.pos_const;
+    for (int b = 0; b < NB; ++b) {
+      rs[b] = wave_sum(rs[b]);
+      if (lane == 0) s_red[wave][b] = rs[b];
+    }
+    __syncthreads();
+    if (tid < NB) {
+      float t = 0.f;
 #pragma unroll
-      for (int r = 0; r < RPW; r += 2) {
-        const int row = row0 + r;
-        if (row + 1 >= N) break;
-        float x0 = acc[r][b], x1 = acc[r + 1][b];
-        const int part = row / a.d;  // 0 q, 1 k, 2 v
-        const int rr = row - part * a.d;
-        const int head = rr / a.hd, dim = rr - head * a.hd;
-        if (part < 2) {
-          const float* cs = a.rope + ((long long)p * (a.hd >> 1) + (dim >> 1)) * 2;
-          const float c = cs[0], sn = cs[1];
-          const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
-          x0 = y0; x1 = y1;
-        }
-        if (part == 0) {
-          y[rr] = x0;
-          y[rr + 1] = x1;
-        } else {
-          const long long off = a.kv.offset(b, a.layer, part - 1, head, p) + dim;
-          if (a.kv_bf16) {
-            uint16_t* kv = (uint16_t*)a.kv.base;
-            kv[off] = f2bf(x0);
-            kv[off + 1] = f2bf(x1);
-          } else {
-            float* kv = (float*)a.kv.base;
-            kv[off] = x0;
-            kv[off + 1] = x1;
+      for (int w = 0; w < kStreamWaves; ++w) t += s_red[w][tid];
+      s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+  for (int i = tid * 4; i < NB * K; i += 64 * kStreamWaves * 4) {
+    const int b = i / K, k = i - b * K;
+    float4 v = *(const float4*)(a.x + (long long)b * a.ldx + k);
+    if (a.gain) {
+      const float r = s_rstd[b];
+      const float4 g = *(const float4*)(a.gain + k);
+      v.x *= r * g.x; v.y *= r * g.y; v.z *= r * g.z; v.w *= r * g.w;
+    }
+    *(float4*)(xs + i) = v;
+  }
+  __syncthreads();
+  if (!live) return;
+
+  float acc[2][NB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  auto consume = [&](int g, const u32x4 (&w)[2][LPG]) {
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int k = g * GROUP + i * SPAN + lane * EPL;
+      if (k < K) {
+        float w0[EPL], w1[EPL];
+        unpack16<BF>(w[0][i], w0);
+        unpack16<BF>(w[1][i], w1);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float xv[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4) {
+            const float4 t = *(const float4*)(xs + b * K + k + e);
+            xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+          }
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            acc[0][b] = fmaf(w0[e], xv[e], acc[0][b]);
+            acc[1][b] = fmaf(w1[e], xv[e], acc[1][b]);
           }
         }
       }
     }
+  };
+  for (int g = 0; g < ng; g += 2) {
+    if (g + 1 < ng) load(g + 1, wb);
+    consume(g, wa);
+    if (g + 1 < ng) {
+      if (g + 2 < ng) load(g + 2, wa);
+      consume(g + 1, wb);
+    }
   }
+
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+  if (lane != 0) return;
+  gemv_epilogue<NB, BF, EPI, 2>(a, row0, 2, acc);
 }
 
 template <int NB, bool BF>
 static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s) {
+  if ((size_t)NB * a.K * sizeof(float) <= 65536) {
+    dim3 grid(((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves);
+    const size_t lds = (size_t)NB * a.K * sizeof(float);
+    const int T = 64 * kStreamWaves;
+    switch (epi) {
+      case EPI_STORE: k_gemv_stream<NB, BF, EPI_STORE><<<grid, T, lds, s>>>(a); break;
+      case EPI_RESID: k_gemv_stream<NB, BF, EPI_RESID><<<grid, T, lds, s>>>(a); break;
+      case EPI_EMB: k_gemv_stream<NB, BF, EPI_EMB><<<grid, T, lds, s>>>(a); break;
+      case EPI_SWIGLU: k_gemv_stream<NB, BF, EPI_SWIGLU><<<grid, T, lds, s>>>(a); break;
+      case EPI_QKV: k_gemv_stream<NB, BF, EPI_QKV><<<grid, T, lds, s>>>(a); break;
+    }
+    return;
+  }
   dim3 grid((a.N + kGemvRows - 1) / kGemvRows);
   size_t lds = (size_t)NB * (size_t)KC * sizeof(float);
   switch (epi) {
@@ -267,49 +429,74 @@ void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Causal decode attention, split over key blocks (flash-decode). Block
-// (split, head, conversation) scores up to 64 keys of one KV page with a
-// group of HD/EPL lanes per key (each lane holds EPL query values), keeps the
-// probabilities in LDS, and accumulates P*V in the same lane layout. Each
-// block writes (o, max, sum) for its split; the last block of a (b, head) to
-// finish, found with an atomic counter, merges the splits in split order, so
-// the result does not depend on block timing.
+// Causal decode attention, split over key ranges (flash-decode). Block
+// (split, head, conversation) owns keys [P*split/NS, P*(split+1)/NS) of the
+// P = pos+1 cached positions (at most kAttnMaxKeys). A group of HD/EPL lanes
+// handles one key (each lane holds EPL query values): the block first scores
+// all its keys into LDS, takes the softmax statistics with block reductions,
+// then accumulates P*V in the same lane layout. With one split the block
+// writes the normalised output; otherwise it writes (o, max, sum) and a second
+// kernel merges the splits in split order, so results do not depend on timing.
 // ---------------------------------------------------------------------------
+constexpr int kAttnMaxKeys = 512;
+
 template <bool KBF, int HD>
-__global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
+__device__ __forceinline__ void load_kv16(const void* base, long long off, float (&v)[KBF ? 8 : 4]) {
+  if constexpr (KBF) {
+    u32x4 t = *(const u32x4*)((const uint16_t*)base + off);
+    v[0] = bf_lo(t.x); v[1] = bf_hi(t.x); v[2] = bf_lo(t.y); v[3] = bf_hi(t.y);
+    v[4] = bf_lo(t.z); v[5] = bf_hi(t.z); v[6] = bf_lo(t.w); v[7] = bf_hi(t.w);
+  } else {
+    f32x4 t = *(const f32x4*)((const float*)base + off);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  }
+}
+
+__device__ __forceinline__ float block_max256(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <bool KBF, int HD>
+__global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   constexpr int EPL = KBF ? 8 : 4;
-  constexpr int G = HD / EPL;  // lanes per key
-  constexpr int KPW = 64 / G;  // keys per wave per pass
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = gridDim.y;
+  constexpr int G = HD / EPL;   // lanes per key
+  constexpr int KPW = 64 / G;   // keys per wave per pass
+  constexpr int KPB = 4 * KPW;  // keys per block per pass
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, H = gridDim.y, NS = gridDim.x;
   const int P = (a.pos ? a.pos[b] : a.pos_const) + 1;
-  const int nact = (P + a.split - 1) / a.split;
-  if (sp >= nact) return;
-  const int k0 = sp * a.split, k1 = min(P, k0 + a.split), n = k1 - k0;
+  const int k0 = (int)((long long)P * sp / NS), k1 = (int)((long long)P * (sp + 1) / NS);
+  const int n = k1 - k0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane % G, g = lane / G;
-  __shared__ float sc[64];
-  __shared__ float so[4 * KPW * HD];
-  __shared__ float s_ml[2];
-  __shared__ int s_last;
+  __shared__ float sc[kAttnMaxKeys];
+  __shared__ float so[KPB * HD];
+  __shared__ float red[4];
 
   float qv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) qv[e] = a.q[(long long)b * a.ldq + h * HD + li * EPL + e] * a.scale;
 
-  for (int base = k0 + wave * KPW; base < k1; base += 4 * KPW) {
+  // scores
+#pragma unroll 4
+  for (int base = k0 + wave * KPW; base < k1; base += KPB) {
     const int key = base + g;
     float d = 0.f;
     if (key < k1) {
-      const long long off = a.kv.offset(b, a.layer, 0, h, key) + li * EPL;
       float kf[EPL];
-      if constexpr (KBF) {
-        u32x4 v = *(const u32x4*)((const uint16_t*)a.kv.base + off);
-        kf[0] = bf_lo(v.x); kf[1] = bf_hi(v.x); kf[2] = bf_lo(v.y); kf[3] = bf_hi(v.y);
-        kf[4] = bf_lo(v.z); kf[5] = bf_hi(v.z); kf[6] = bf_lo(v.w); kf[7] = bf_hi(v.w);
-      } else {
-        f32x4 v = *(const f32x4*)((const float*)a.kv.base + off);
-        kf[0] = v.x; kf[1] = v.y; kf[2] = v.z; kf[3] = v.w;
-      }
+      load_kv16<KBF, HD>(a.kv.base, a.kv.offset(b, a.layer, 0, h, key) + li * EPL, kf);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], kf[e], d);
     }
@@ -318,36 +505,27 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
     if (key < k1 && li == 0) sc[key - k0] = d;
   }
   __syncthreads();
-  if (wave == 0) {
-    const float s = lane < n ? sc[lane] : -INFINITY;
-    const float m = wave_max(s);
-    const float p = lane < n ? expf(s - m) : 0.f;
-    const float l = wave_sum(p);
-    if (lane < n) sc[lane] = p;
-    if (lane == 0) {
-      s_ml[0] = m;
-      s_ml[1] = l;
-    }
+  float m = -INFINITY;
+  for (int i = tid; i < n; i += 256) m = fmaxf(m, sc[i]);
+  m = block_max256(m, red);
+  float l = 0.f;
+  for (int i = tid; i < n; i += 256) {
+    const float p = expf(sc[i] - m);
+    sc[i] = p;
+    l += p;
   }
-  __syncthreads();
+  l = block_sum256(l, red);  // contains the barrier that publishes sc
 
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int base = k0 + wave * KPW; base < k1; base += 4 * KPW) {
+#pragma unroll 4
+  for (int base = k0 + wave * KPW; base < k1; base += KPB) {
     const int key = base + g;
     if (key < k1) {
       const float p = sc[key - k0];
-      const long long off = a.kv.offset(b, a.layer, 1, h, key) + li * EPL;
       float vf[EPL];
-      if constexpr (KBF) {
-        u32x4 v = *(const u32x4*)((const uint16_t*)a.kv.base + off);
-        vf[0] = bf_lo(v.x); vf[1] = bf_hi(v.x); vf[2] = bf_lo(v.y); vf[3] = bf_hi(v.y);
-        vf[4] = bf_lo(v.z); vf[5] = bf_hi(v.z); vf[6] = bf_lo(v.w); vf[7] = bf_hi(v.w);
-      } else {
-        f32x4 v = *(const f32x4*)((const float*)a.kv.base + off);
-        vf[0] = v.x; vf[1] = v.y; vf[2] = v.z; vf[3] = v.w;
-      }
+      load_kv16<KBF, HD>(a.kv.base, a.kv.offset(b, a.layer, 1, h, key) + li * EPL, vf);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
     }
@@ -355,45 +533,47 @@ __global__ __launch_bounds__(256) void k_attn_decode(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) so[(wave * KPW + g) * HD + li * EPL + e] = acc[e];
   __syncthreads();
-
-  float* part = a.part + ((long long)(b * H + h) * a.max_splits) * (HD + 2);
   if (tid < HD) {
     float o = 0.f;
-    for (int i = 0; i < 4 * KPW; ++i) o += so[i * HD + tid];
-    part[(long long)sp * (HD + 2) + tid] = o;
-    if (tid == 0) {
-      part[(long long)sp * (HD + 2) + HD] = s_ml[0];
-      part[(long long)sp * (HD + 2) + HD + 1] = s_ml[1];
+#pragma unroll 4
+    for (int i = 0; i < KPB; ++i) o += so[i * HD + tid];
+    if (NS == 1) {
+      a.out[(long long)b * a.ldo + h * HD + tid] = o / l;
+    } else {
+      float* part = a.part + ((long long)(b * H + h) * NS + sp) * (HD + 2);
+      part[tid] = o;
+      if (tid == 0) {
+        part[HD] = m;
+        part[HD + 1] = l;
+      }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(&a.counters[b * H + h], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (old == nact - 1);
+}
+
+template <int HD>
+__global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a, int NS) {
+  const int h = blockIdx.x, b = blockIdx.y, H = gridDim.x, t = threadIdx.x;
+  const float* part = a.part + (long long)(b * H + h) * NS * (HD + 2);
+  float M = -INFINITY;
+  for (int i = 0; i < NS; ++i) M = fmaxf(M, part[i * (HD + 2) + HD]);
+  float L = 0.f, o = 0.f;
+  for (int i = 0; i < NS; ++i) {
+    const float* pi = part + i * (HD + 2);
+    const float w = pi[HD + 1] > 0.f ? expf(pi[HD] - M) : 0.f;
+    L = fmaf(w, pi[HD + 1], L);
+    o = fmaf(w, pi[t], o);
   }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid < HD) {
-    float M = -INFINITY;
-    for (int i = 0; i < nact; ++i)
-      M = fmaxf(M, __hip_atomic_load(part + (long long)i * (HD + 2) + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    float L = 0.f, o = 0.f;
-    for (int i = 0; i < nact; ++i) {
-      const float* pi = part + (long long)i * (HD + 2);
-      const float w = expf(__hip_atomic_load(pi + HD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - M);
-      L = fmaf(w, __hip_atomic_load(pi + HD + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), L);
-      o = fmaf(w, __hip_atomic_load(pi + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), o);
-    }
-    a.out[(long long)b * a.ldo + h * HD + tid] = o / L;
-  }
-  if (tid == 0) __hip_atomic_store(&a.counters[b * H + h], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a.out[(long long)b * a.ldo + h * HD + t] = o / L;
 }
 
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s) {
-  dim3 grid(a.max_splits, H, B);
-#define MOSHI_ATTN(KB, HDV) k_attn_decode<KB, HDV><<<grid, 256, 0, s>>>(a)
+  const int NS = a.max_splits;
+  dim3 grid(NS, H, B);
+#define MOSHI_ATTN(KB, HDV)                                                   \
+  do {                                                                        \
+    k_attn_split<KB, HDV><<<grid, 256, 0, s>>>(a);                            \
+    if (NS > 1) k_attn_merge<HDV><<<dim3(H, B), HDV, 0, s>>>(a, NS);          \
+  } while (0)
   if (kv_bf16) {
     if (hd == 32) MOSHI_ATTN(true, 32);
     else if (hd == 64) MOSHI_ATTN(true, 64);

@@ -61,10 +61,10 @@ struct AttnArgs {
   int layer;
   const int* pos;  // [B]: keys 0..pos[b]; null -> pos_const
   int pos_const;
-  int split;       // keys per block (<= 64)
+  int split;       // unused
   float* part;     // [B][H][max_splits][hd + 2]
-  int max_splits;
-  int* counters;   // [B][H], zero between uses
+  int max_splits;  // key-range splits per (b, head); P / max_splits <= 512 keys
+  int* counters;   // unused
   float* out;      // [B][ldo]
   int ldo;
   float scale;

@@ -1,0 +1,77 @@
+"""GPU parity on the mid configuration (d=1024, 8 temporal layers, 32000-word text
+vocabulary, 7B-shape depth), float32 and bf16 weights: a 375-frame prompt
+prefilled into the KV cache, then 125 frames teacher-forced on the oracle's greedy
+tokens; plus a 3750-frame context that spreads the decode attention over all of
+its key splits."""
+import numpy as np
+import pytest
+
+from oracle import Oracle, Session
+from parity_util import compare_frame, prompt_V, rel_l2
+from synth import config, generate_weights
+
+pytestmark = pytest.mark.gpu
+
+TOLS = {"mid_f32": 1e-4, "mid_bf16": 1e-2}
+
+
+def oracle_prefilled(model, V, P):
+    sess = Session(model)
+    model.temporal(np.concatenate([model.initial_frame[None], V[:P - 1]]), 0, sess.cache)
+    sess.pos = P
+    sess.prev = V[P - 1].copy()
+    return sess
+
+
+def run_case(name, P, n, tol_scale=1.0):
+    from full_duplex_speech_amd import Moshi
+    cfg = config(name)
+    tol = TOLS[name] * tol_scale
+    w = generate_weights(cfg, seed=0)
+    V = prompt_V(cfg, 0, P + n)
+    model = Oracle(cfg, w)
+    sess = oracle_prefilled(model, V, P)
+    eng = Moshi(cfg, max_batch=1)
+    eng.load_weights(w)
+    eng.forward_teacher_forced(V[None, :P], fill_kv=True, skip_depth=True, logits=False, loss=False)
+    worst, checked, total = 0.0, 0, 0
+    for s in range(n):
+        own, lt, la = sess.step(V[P + s, 9:])
+        tok, glt, gla = eng.step(V[P + s, 9:][None], force=own[None], logits=True)
+        wv, c, t = compare_frame(cfg, P + s, own, lt, la, tok[0], glt[0], gla[0], tol)
+        worst, checked, total = max(worst, wv), checked + c, total + t
+    eng.close()
+    print(f"{name} P={P}: {n} frames, worst rel-L2 {worst:.2e}, tokens checked {checked}/{total}")
+    return worst
+
+
+@pytest.mark.parametrize("name", ["mid_f32", "mid_bf16"])
+def test_mid_prompt_then_generate(name):
+    cfg = config(name)
+    run_case(name, cfg.prompt_frames, cfg.gen_frames)
+
+
+def test_mid_long_context_all_splits():
+    run_case("mid_bf16", 3750, 3)
+
+
+def test_mid_teacher_forced_logits_and_loss():
+    from full_duplex_speech_amd import Moshi
+    from oracle import cross_entropy_loss
+    cfg = config("mid_bf16")
+    w = generate_weights(cfg, seed=0)
+    B, S = 2, 24
+    V = np.stack([prompt_V(cfg, b, S) for b in range(B)])
+    model = Oracle(cfg, w)
+    eng = Moshi(cfg, max_batch=B)
+    eng.load_weights(w)
+    lt, la, loss = eng.forward_teacher_forced(V)
+    eng.close()
+    rt, ra = zip(*[model.forward_teacher_forced(V[b])[:2] for b in range(B)])
+    rt, ra = np.stack(rt), np.stack(ra)
+    worst = max(rel_l2(lt[b, s], rt[b, s]) for b in range(B) for s in range(S))
+    worst = max(worst, max(rel_l2(la[b, s, j], ra[b, s, j]) for b in range(B) for s in range(S) for j in range(8)))
+    assert worst <= 1e-2
+    ref = cross_entropy_loss(cfg, V, rt, ra)
+    for k in ("ce_text", "ce_audio", "ce_total"):
+        assert loss[k] == pytest.approx(ref[k], rel=1e-3)
