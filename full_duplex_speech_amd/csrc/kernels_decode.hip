@@ -14,6 +14,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "moshi_internal.h"
 
 namespace moshi {
@@ -378,20 +380,274 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_stream(GemvArgs a) {
   gemv_epilogue<NB, BF, EPI, 2>(a, row0, 2, acc);
 }
 
+// Persistent variant of the streaming GEMV: a grid of about two blocks per CU;
+// every wave walks a sequence of units (row pair, K-group of LPG wave-wide
+// loads per row) assigned round-robin over all waves. The weight registers of
+// a unit are refilled with the next unit's data right after they are consumed,
+// so each lane keeps ~2*LPG 16-byte loads in flight for the whole kernel. The
+// steady-state loop has no data-dependent branches: addresses past the end of
+// a row or of the matrix are clamped to valid weights whose products meet
+// zero-padded inputs or are never stored, and every operand the epilogue
+// needs (residual, embedding row, RoPE angle) is loaded before the refills,
+// so the compiler never has to drain the load queue.
+template <int NB, bool BF, int EPI, int LPG>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) {
+  constexpr int EPL = WLoad<BF>::EPL, SPAN = 64 * EPL, GROUP = SPAN * LPG;
+  constexpr int ESZ = BF ? 2 : 4;
+  extern __shared__ float4 xs4[];  // [NB][KP], zero past K
+  float* xs = (float*)xs4;
+  __shared__ float s_red[kStreamWaves][NB];
+  __shared__ float s_rstd[NB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+  const int ng = (K + GROUP - 1) / GROUP;
+  const int KP = ng * GROUP;
+  const int npairs = (N + 1) / 2;
+  const int nw = gridDim.x * kStreamWaves;
+  const int gw = blockIdx.x * kStreamWaves + wave;
+  const int mine = gw < npairs ? (npairs - 1 - gw) / nw + 1 : 0;
+  const int units = mine * ng;
+  const char* Wb = (const char*)a.W;
+
+  // per-kernel epilogue constants
+  int pos_b[NB], page_b[NB], tok_b[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    pos_b[b] = 0;
+    page_b[b] = 0;
+    tok_b[b] = 0;
+    if constexpr (EPI == EPI_QKV) {
+      pos_b[b] = a.pos ? a.pos[b] : a.pos_const;
+      page_b[b] = a.kv.page_table ? a.kv.page_table[b * a.kv.pt_stride + pos_b[b] / a.kv.pf] : b;
+    }
+    if constexpr (EPI == EPI_EMB) tok_b[b] = min(max(a.tok[b * a.tok_stride + a.tok_col], 0), a.tok_rows - 1);
+  }
+
+  u32x4 w0[LPG], w1[LPG];
+  auto load_slot = [&](int pair, int g, int i, u32x4& d0, u32x4& d1) {
+    const int k = min(g * GROUP + i * SPAN + lane * EPL, K - EPL);
+    const int r0 = min(pair * 2, N - 1), r1 = min(pair * 2 + 1, N - 1);
+    d0 = __builtin_nontemporal_load((const u32x4*)(Wb + ((long long)r0 * K + k) * ESZ));
+    d1 = __builtin_nontemporal_load((const u32x4*)(Wb + ((long long)r1 * K + k) * ESZ));
+  };
+  if (units > 0) {
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) load_slot(gw, 0, i, w0[i], w1[i]);
+  }
+
+  // prologue: RMSNorm statistics and the normalised, zero-padded inputs in LDS
+  if (a.gain) {
+    float rs[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) rs[b] = 0.f;
+    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float4 v = *(const float4*)(a.x + (long long)b * a.ldx + k);
+        rs[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      rs[b] = wave_sum(rs[b]);
+      if (lane == 0) s_red[wave][b] = rs[b];
+    }
+    __syncthreads();
+    if (tid < NB) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < kStreamWaves; ++w) t += s_red[w][tid];
+      s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+  for (int i = tid * 4; i < NB * KP; i += 64 * kStreamWaves * 4) {
+    const int b = i / KP, k = i - b * KP;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < K) {
+      v = *(const float4*)(a.x + (long long)b * a.ldx + k);
+      if (a.gain) {
+        const float r = s_rstd[b];
+        const float4 g = *(const float4*)(a.gain + k);
+        v.x *= r * g.x; v.y *= r * g.y; v.z *= r * g.z; v.w *= r * g.w;
+      }
+    }
+    xs4[i >> 2] = v;
+  }
+  __syncthreads();
+  if (units == 0) return;
+
+  float acc[2][NB];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+
+  // epilogue operands of a row pair (residual, embedding row, RoPE angle); they
+  // are loaded one row pair ahead and carried, so their loads are never
+  // waited on right after the weight refills
+  auto load_pre = [&](int pair, float (&pre)[2][NB]) {
+    const int r0 = min(pair * 2, N - 1), r1 = min(pair * 2 + 1, N - 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      pre[0][b] = 0.f;
+      pre[1][b] = 0.f;
+      if constexpr (EPI == EPI_RESID) {
+        pre[0][b] = a.y[(long long)b * a.ldy + r0];
+        pre[1][b] = a.y[(long long)b * a.ldy + r1];
+      }
+      if constexpr (EPI == EPI_EMB) {
+        pre[0][b] = load_w1(a.emb, (long long)tok_b[b] * N + r0, BF);
+        pre[1][b] = load_w1(a.emb, (long long)tok_b[b] * N + r1, BF);
+      }
+      if constexpr (EPI == EPI_QKV) {
+        // rows of q and k rotate; both rows of the pair share the angle
+        const int dim = (r0 % a.d) % a.hd;
+        const float* cs = a.rope + ((long long)pos_b[b] * (a.hd >> 1) + (dim >> 1)) * 2;
+        pre[0][b] = cs[0];
+        pre[1][b] = cs[1];
+      }
+    }
+  };
+  float pre[2][NB], pre_n[2][NB];
+  load_pre(gw, pre);
+
+  auto unit = [&](int pair, int g, int npair, int ngrp, bool refill) {
+    if (refill) load_pre(npair, pre_n);
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int k = g * GROUP + i * SPAN + lane * EPL;
+      float f0[EPL], f1[EPL];
+      unpack16<BF>(w0[i], f0);
+      unpack16<BF>(w1[i], f1);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float xv[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; e += 4) {
+          const float4 t = xs4[(b * KP + k + e) >> 2];
+          xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          acc[0][b] = fmaf(f0[e], xv[e], acc[0][b]);
+          acc[1][b] = fmaf(f1[e], xv[e], acc[1][b]);
+        }
+      }
+      if (refill) load_slot(npair, ngrp, i, w0[i], w1[i]);
+    }
+    if (g == ng - 1) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[r][b] = wave_sum(acc[r][b]);
+      const int row = pair * 2;
+      if (lane < NB) {
+        // lane b stores conversation b's outputs
+        const int b = lane;
+        float s0 = acc[0][0], s1 = acc[1][0], p0 = pre[0][0], p1 = pre[1][0];
+        int pos = pos_b[0], page = page_b[0];
+#pragma unroll
+        for (int bb = 1; bb < NB; ++bb)
+          if (bb == b) {
+            s0 = acc[0][bb]; s1 = acc[1][bb]; p0 = pre[0][bb]; p1 = pre[1][bb];
+            pos = pos_b[bb]; page = page_b[bb];
+          }
+        float* y = a.y + (long long)b * a.ldy;
+        if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
+          y[row] = s0 + p0;
+          if (row + 1 < N) y[row + 1] = s1 + p1;
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          y[row >> 1] = s0 / (1.0f + expf(-s0)) * s1;
+        } else if constexpr (EPI == EPI_QKV) {
+          const int part = row / a.d;
+          const int rr = row - part * a.d;
+          const int head = rr / a.hd, dim = rr - head * a.hd;
+          float x0 = s0, x1 = s1;
+          if (part < 2) {
+            x0 = s0 * p0 - s1 * p1;
+            x1 = s0 * p1 + s1 * p0;
+          }
+          if (part == 0) {
+            y[rr] = x0;
+            y[rr + 1] = x1;
+          } else {
+            const long long off = (long long)page * a.kv.page_stride +
+                                  ((long long)((a.layer * 2 + part - 1) * a.kv.n_heads + head) * a.kv.pf +
+                                   (pos % a.kv.pf)) * a.kv.hd + dim;
+            if (a.kv_bf16) {
+              const uint32_t v = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
+              *(uint32_t*)((uint16_t*)a.kv.base + off) = v;
+            } else {
+              *(float2*)((float*)a.kv.base + off) = make_float2(x0, x1);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[r][b] = 0.f;
+    }
+    if (refill && ngrp == 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) pre[r][b] = pre_n[r][b];
+    }
+  };
+
+  int pair = gw, g = 0;
+  for (int u = 0; u < units - 1; ++u) {
+    int npair = pair, ngrp = g + 1;
+    if (ngrp == ng) {
+      ngrp = 0;
+      npair += nw;
+    }
+    unit(pair, g, npair, ngrp, true);
+    pair = npair;
+    g = ngrp;
+  }
+  unit(pair, g, pair, g, false);
+}
+
+static int device_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
 template <int NB, bool BF>
 static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s) {
   if ((size_t)NB * a.K * sizeof(float) <= 65536) {
-    dim3 grid(((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves);
+    const int need = ((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
+    dim3 grid(std::min(need, 2 * device_cus()));
     const size_t lds = (size_t)NB * a.K * sizeof(float);
     const int T = 64 * kStreamWaves;
-    switch (epi) {
-      case EPI_STORE: k_gemv_stream<NB, BF, EPI_STORE><<<grid, T, lds, s>>>(a); break;
-      case EPI_RESID: k_gemv_stream<NB, BF, EPI_RESID><<<grid, T, lds, s>>>(a); break;
-      case EPI_EMB: k_gemv_stream<NB, BF, EPI_EMB><<<grid, T, lds, s>>>(a); break;
-      case EPI_SWIGLU: k_gemv_stream<NB, BF, EPI_SWIGLU><<<grid, T, lds, s>>>(a); break;
-      case EPI_QKV: k_gemv_stream<NB, BF, EPI_QKV><<<grid, T, lds, s>>>(a); break;
+    constexpr int EPL = WLoad<BF>::EPL;
+    const int slots = (a.K + 64 * EPL - 1) / (64 * EPL);
+    const int lpg = slots <= 2 ? 2 : (slots <= 4 ? 4 : 8);
+    const int KP = ((a.K + 64 * EPL * lpg - 1) / (64 * EPL * lpg)) * 64 * EPL * lpg;
+    const size_t lds_p = (size_t)NB * KP * sizeof(float);
+#define MOSHI_GP(E, L) k_gemv_persist<NB, BF, E, L><<<grid, T, lds_p, s>>>(a)
+#define MOSHI_GPL(E) (lpg == 2 ? MOSHI_GP(E, 2) : (lpg == 4 ? MOSHI_GP(E, 4) : MOSHI_GP(E, 8)))
+    if (lds_p <= 65536) {
+      switch (epi) {
+        case EPI_STORE: MOSHI_GPL(EPI_STORE); break;
+        case EPI_RESID: MOSHI_GPL(EPI_RESID); break;
+        case EPI_EMB: MOSHI_GPL(EPI_EMB); break;
+        case EPI_SWIGLU: MOSHI_GPL(EPI_SWIGLU); break;
+        case EPI_QKV: MOSHI_GPL(EPI_QKV); break;
+      }
+      return;
     }
-    return;
+#undef MOSHI_GPL
+#undef MOSHI_GP
+    (void)lds;
   }
   dim3 grid((a.N + kGemvRows - 1) / kGemvRows);
   size_t lds = (size_t)NB * (size_t)KC * sizeof(float);
