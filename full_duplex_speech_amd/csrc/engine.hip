@@ -117,6 +117,8 @@ int validate(const moshi_config& c, std::string& msg) {
   if (c.page_frames != 8 && c.page_frames != 16 && c.page_frames != 32 && c.page_frames != 64)
     return bad("page_frames must be 8, 16, 32 or 64");
   if (c.n_pages < 0 || c.max_tf_tokens < 0) return bad("n_pages and max_tf_tokens must be >= 0");
+  if ((c.ctx_max + c.page_frames - 1) / c.page_frames > kMaxPagesPerConv)
+    return bad("ctx_max / page_frames must be at most 512 pages");
   return MOSHI_OK;
 }
 

@@ -806,6 +806,126 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnArgs a) {
   }
 }
 
+// Decode attention over the paged temporal cache. Block (split, head,
+// conversation) owns keys [P*split/NS, P*(split+1)/NS) of the P = pos+1
+// positions; NS is chosen so that the grid has about one block per CU. The
+// block looks its page ids up once, then walks its keys in passes of 4*KPW;
+// each group of G lanes keeps its own online-softmax state (running max, sum,
+// P*V accumulator) over the keys it saw, with K and V of a chunk of passes
+// requested together, so the key loop has no block barriers. The 4*KPW states
+// are merged through LDS at the end; with NS > 1 the block writes (o, max, sum)
+// and k_attn_merge combines the splits in split order.
+constexpr int kAttnWaves = 4;
+constexpr int kAttnPasses = 8;
+constexpr int kMaxAttnSplits = 16;
+
+template <bool KBF, int HD>
+__global__ __launch_bounds__(64 * kAttnWaves) void k_attn_range(AttnArgs a) {
+  constexpr int EPL = KBF ? 8 : 4;
+  constexpr int ESZ = KBF ? 2 : 4;
+  constexpr int G = HD / EPL;
+  constexpr int KPW = 64 / G;
+  constexpr int KPB = kAttnWaves * KPW;
+  constexpr int NST = KPB;  // lane-group states
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z, NS = gridDim.x, H = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane % G, g = lane / G;
+  const int P = a.pos[b] + 1;
+  const int k0 = (int)((long long)P * sp / NS), k1 = (int)((long long)P * (sp + 1) / NS);
+  const KvView& kv = a.kv;
+  __shared__ int pages[kMaxPagesPerConv];
+  __shared__ float st_m[NST], st_l[NST];
+  __shared__ float st_o[NST * HD];
+  const int pg0 = k0 / kv.pf, pg1 = k1 > k0 ? (k1 - 1) / kv.pf : pg0;
+  for (int i = pg0 + tid; i <= pg1; i += 64 * kAttnWaves) pages[i - pg0] = kv.page_table[b * kv.pt_stride + i];
+
+  float qv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) qv[e] = a.q[(long long)b * a.ldq + h * HD + li * EPL + e] * a.scale;
+  __syncthreads();
+
+  const long long head_off = (long long)((a.layer * 2) * kv.n_heads + h) * kv.pf * kv.hd;
+  const long long v_off = (long long)kv.n_heads * kv.pf * kv.hd * ESZ;  // K block -> V block, bytes
+  float m = -INFINITY, l = 0.f, acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+
+  for (int c0 = k0; c0 < k1; c0 += KPB * kAttnPasses) {
+    u32x4 kr[kAttnPasses], vr[kAttnPasses];
+#pragma unroll
+    for (int i = 0; i < kAttnPasses; ++i) {
+      const int key = min(c0 + i * KPB + wave * KPW + g, k1 - 1);
+      const long long off = (long long)pages[key / kv.pf - pg0] * kv.page_stride + head_off +
+                            (long long)(key % kv.pf) * kv.hd + li * EPL;
+      const char* base = (const char*)kv.base + off * ESZ;
+      kr[i] = *(const u32x4*)base;
+      vr[i] = *(const u32x4*)(base + v_off);
+    }
+    asm volatile("" ::: "memory");  // keep every K and V request ahead of the math
+    float sc[kAttnPasses];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kAttnPasses; ++i) {
+      float kf[EPL];
+      unpack16<KBF>(kr[i], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], kf[e], d);
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+      sc[i] = (c0 + i * KPB + wave * KPW + g < k1) ? d : -INFINITY;
+      cmax = fmaxf(cmax, sc[i]);
+    }
+    const float mn = fmaxf(m, cmax);
+    if (mn != -INFINITY) {
+      const float alpha = expf(m - mn);  // m = -inf -> 0
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < kAttnPasses; ++i) {
+        const float p = expf(sc[i] - mn);  // keys outside the range -> 0
+        l += p;
+        float vf[EPL];
+        unpack16<KBF>(vr[i], vf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+      }
+      m = mn;
+    }
+  }
+  const int st = wave * KPW + g;
+  if (li == 0) {
+    st_m[st] = m;
+    st_l[st] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) st_o[st * HD + li * EPL + e] = acc[e];
+  __syncthreads();
+  if (tid < HD) {
+    float M = -INFINITY;
+    for (int i = 0; i < NST; ++i) M = fmaxf(M, st_m[i]);
+    float L = 0.f, o = 0.f;
+    if (M != -INFINITY) {
+      for (int i = 0; i < NST; ++i) {
+        const float w = st_m[i] == -INFINITY ? 0.f : expf(st_m[i] - M);
+        L = fmaf(w, st_l[i], L);
+        o = fmaf(w, st_o[i * HD + tid], o);
+      }
+    }
+    if (NS == 1) {
+      a.out[(long long)b * a.ldo + h * HD + tid] = o / L;
+    } else {
+      float* part = a.part + ((long long)(b * H + h) * NS + sp) * (HD + 2);
+      part[tid] = o;
+      if (tid == 0) {
+        part[HD] = M;
+        part[HD + 1] = L;
+      }
+    }
+  }
+}
+
 template <int HD>
 __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a, int NS) {
   const int h = blockIdx.x, b = blockIdx.y, H = gridDim.x, t = threadIdx.x;
@@ -823,6 +943,28 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a, int NS) {
 }
 
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s) {
+  if (a.kv.page_table && a.pos) {
+    // temporal cache: about one block per CU over (split, head, conversation)
+    const int NS = std::max(1, std::min(std::min(a.max_splits, kMaxAttnSplits), 256 / (B * H)));
+    dim3 grid(NS, H, B);
+    const int T = 64 * kAttnWaves;
+#define MOSHI_AR(KB, HDV)                                                  \
+  do {                                                                     \
+    k_attn_range<KB, HDV><<<grid, T, 0, s>>>(a);                           \
+    if (NS > 1) k_attn_merge<HDV><<<dim3(H, B), HDV, 0, s>>>(a, NS);       \
+  } while (0)
+    if (kv_bf16) {
+      if (hd == 32) MOSHI_AR(true, 32);
+      else if (hd == 64) MOSHI_AR(true, 64);
+      else MOSHI_AR(true, 128);
+    } else {
+      if (hd == 32) MOSHI_AR(false, 32);
+      else if (hd == 64) MOSHI_AR(false, 64);
+      else MOSHI_AR(false, 128);
+    }
+#undef MOSHI_AR
+    return;
+  }
   const int NS = a.max_splits;
   dim3 grid(NS, H, B);
 #define MOSHI_ATTN(KB, HDV)                                                   \
@@ -851,17 +993,24 @@ template <bool BF>
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   const int b = blockIdx.y;
   const int i = blockIdx.x * 256 + threadIdx.x;
+  int t[kStreams];
+#pragma unroll
+  for (int k = 0; k < kStreams; ++k) t[k] = a.frames[b * kStreams + k];
   if (i >= a.d) return;
-  float s = 0.f;
+  float v[kStreams];
+#pragma unroll
   for (int k = 0; k < kStreams; ++k) {
-    int t = a.frames[b * kStreams + k];
-    if (t < 0 || t >= a.rows[k]) {
+    int tk = t[k];
+    if (tk < 0 || tk >= a.rows[k]) {
       if (i == 0) atomicOr(a.err, 1);
-      t = a.rows[k] - 1;
+      tk = a.rows[k] - 1;
     }
-    const long long idx = (a.row0[k] + t) * (long long)a.d + i;
-    s += BF ? bf2f(((const uint16_t*)a.table)[idx]) : ((const float*)a.table)[idx];
+    const long long idx = (a.row0[k] + tk) * (long long)a.d + i;
+    v[k] = BF ? bf2f(((const uint16_t*)a.table)[idx]) : ((const float*)a.table)[idx];
   }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < kStreams; ++k) s += v[k];
   a.h[(long long)b * a.d + i] = s;
 }
 
@@ -883,29 +1032,40 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_argmax(ArgmaxArgs a) {
+__global__ __launch_bounds__(1024) void k_argmax(ArgmaxArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* l = a.logits + (long long)b * a.ld;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = tid; i < a.n; i += 256) {
-    const float v = l[i];
-    if (v > bv) {
-      bv = v;
-      bi = i;
+  // 8 independent loads in flight per thread; indices increase within a thread,
+  // so a strict '>' keeps the lowest index of equal values
+  for (int base = 0; base < a.n; base += 1024 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 1024 + tid;
+      v[u] = i < a.n ? l[i] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + u * 1024 + tid;
+      if (v[u] > bv) {
+        bv = v[u];
+        bi = i;
+      }
     }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
-  __shared__ float sv[4];
-  __shared__ int si[4];
+  __shared__ float sv[16];
+  __shared__ int si[16];
   if (lane == 0) {
     sv[wave] = bv;
     si[wave] = bi;
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < 4; ++w) better(bv, bi, sv[w], si[w]);
+    for (int w = 1; w < 16; ++w) better(bv, bi, sv[w], si[w]);
     int own = (bi == 0x7fffffff) ? 0 : bi;
     if (a.pad_after && a.pos[b] < a.delay) own = a.pad_id;
     a.out_tok[b * kSlots + a.slot] = own;
@@ -913,7 +1073,7 @@ __global__ __launch_bounds__(256) void k_argmax(ArgmaxArgs a) {
   }
 }
 
-void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s) { k_argmax<<<B, 256, 0, s>>>(a); }
+void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s) { k_argmax<<<B, 1024, 0, s>>>(a); }
 
 // ---------------------------------------------------------------------------
 // End of a frame: V_s = (Moshi's slots fed forward) ++ (user's slots) becomes

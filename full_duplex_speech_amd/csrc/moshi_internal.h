@@ -9,6 +9,7 @@ namespace moshi {
 constexpr int kMaxBatch = 8;
 constexpr int kSlots = 9;     // Moshi's own slots per frame: text + 8 codebooks
 constexpr int kStreams = 17;  // slots per frame
+constexpr int kMaxPagesPerConv = 512;  // ctx_max / page_frames
 
 // Location of one key/value vector in a paged cache. A page holds `pf`
 // consecutive positions of one conversation for every layer, laid out
