@@ -91,6 +91,10 @@ struct Plan {
   size_t hd = 0, dq = 0, dattn = 0, dinter = 0, part_d = 0, audio_logits = 0;
   // teacher-forced
   size_t tf_tokens = 0, tf_ce = 0, tf_res = 0;
+  long long tf_max = 0;
+  bool tf_mfma = false;  // matrix-core teacher-forced pass (bf16 models)
+  size_t tf_H = 0, tf_Xn = 0, tf_I = 0, tf_Q = 0, tf_O = 0, tf_text = 0;
+  size_t tf_U = 0, tf_Xd = 0, tf_DQ = 0, tf_DK = 0, tf_DV = 0, tf_DO = 0, tf_DI = 0, tf_audio = 0;
   size_t staging = 0, staging_bytes = 0;
 };
 
@@ -212,6 +216,28 @@ Plan make_plan(const moshi_config& c) {
   p.tf_tokens = p.take((size_t)tf * kStreams * 4);
   p.tf_ce = p.take((size_t)tf * kSlots * 8);
   p.tf_res = p.take(32 * 8);
+  p.tf_max = tf;
+  // matrix-core pass: bf16 weights, GEMM K dims multiple of 32, head dims the
+  // flash/depth attention kernels support
+  p.tf_mfma = p.bf && d % 32 == 0 && F % 32 == 0 && dd % 32 == 0 && Fd % 32 == 0 && (hdt == 64 || hdt == 128) &&
+              hdd <= 64;
+  if (p.tf_mfma) {
+    const size_t T = (size_t)tf;
+    p.tf_H = p.take(T * d * 4);
+    p.tf_Xn = p.take(T * d * 2);
+    p.tf_I = p.take(T * F * 2);
+    p.tf_Q = p.take(T * d * 2);
+    p.tf_O = p.take(T * d * 2);
+    p.tf_text = p.take(T * c.vocab_text * 4);
+    p.tf_U = p.take(T * c.n_q * dd * 4);
+    p.tf_Xd = p.take(T * dd * 2);
+    p.tf_DQ = p.take(T * c.n_q * dd * 2);
+    p.tf_DK = p.take(T * c.n_q * dd * 2);
+    p.tf_DV = p.take(T * c.n_q * dd * 2);
+    p.tf_DO = p.take(T * dd * 2);
+    p.tf_DI = p.take(T * Fd * 2);
+    p.tf_audio = p.take(T * c.n_q * c.codebook * 4);
+  }
   p.staging_bytes = 64ull << 20;
   p.staging = p.take(p.staging_bytes);
   p.total = (p.total + 255) & ~(size_t)255;
@@ -232,6 +258,7 @@ struct moshi_ctx {
   size_t n_loaded = 0;
   bool ready = false;
   bool use_graph = true;
+  bool tf_steps = false;  // teacher-forced pass as forced frame steps even for bf16 models
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
   // host mirrors
   std::vector<int> pos_h;
@@ -553,6 +580,181 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   HIPCHECK(hipGetLastError());
 }
 
+// Teacher-forced pass on matrix cores (bf16 models): every linear map is one
+// GEMM over the B*S frames; attention is causal flash attention over the KV
+// pages of conversations 0..B-1; the Depth Transformer runs layer by layer over
+// its 8 positions, which teacher forcing makes known in advance.
+void enqueue_tf_mfma(moshi_ctx* c, const int* tok, int B, int S, bool depth, float* text_out, float* audio_out,
+                     bool want_loss) {
+  const moshi_config& g = c->cfg;
+  const Plan& p = c->plan;
+  hipStream_t s = c->stream;
+  const long long M = (long long)B * S;
+  const int d = g.d_t, F = g.ffn_t, dd = g.d_d, Fd = g.ffn_d, NQ = g.n_q;
+  const int hdt = d / g.n_heads_t, hdd = dd / g.n_heads_d;
+  float* H = c->at<float>(p.tf_H);
+  uint16_t* Xn = c->at<uint16_t>(p.tf_Xn);
+  uint16_t* I = c->at<uint16_t>(p.tf_I);
+  uint16_t* Q = c->at<uint16_t>(p.tf_Q);
+  uint16_t* O = c->at<uint16_t>(p.tf_O);
+  float* text = text_out ? text_out : c->at<float>(p.tf_text);
+  float* audio = audio_out ? audio_out : c->at<float>(p.tf_audio);
+
+  EmbedArgs ea{};
+  ea.table = c->ws + p.emb_t;
+  ea.row0 = c->at<long long>(p.meta_row0);
+  ea.rows = c->at<int>(p.meta_rows);
+  ea.h = H;
+  ea.d = d;
+  ea.err = c->at<int>(p.st_err);
+  launch_tf_embed(ea, tok, M, S, g.vocab_text, g.codebook, s);
+
+  const KvView tkv = temporal_kv(c);
+  auto gemm = [&](const void* W, const uint16_t* X, long long ldx, int N, int K) {
+    GemmArgs a{};
+    a.W = (const uint16_t*)W;
+    a.X = X;
+    a.ldx = ldx;
+    a.M = (int)M;
+    a.N = N;
+    a.K = K;
+    return a;
+  };
+  for (int l = 0; l < g.n_layers_t; ++l) {
+    const LayerW& w = p.lt[l];
+    launch_rmsnorm_f16(H, d, c->at<float>(w.attn_norm), g.norm_eps, d, Xn, d, M, s);
+    GemmArgs q = gemm(c->ws + w.wqkv, Xn, d, 3 * d, d);
+    q.d = d;
+    q.hd = hdt;
+    q.S = S;
+    q.pos_const = -1;
+    q.rope = c->at<float>(p.rope_t);
+    q.q = Q;
+    q.ldq = d;
+    q.kv = tkv;
+    q.kv_paged = 1;
+    q.layer = l;
+    launch_gemm_bf16(q, TF_QKV, s);
+    FlashArgs fa{};
+    fa.q = Q;
+    fa.ldq = d;
+    fa.kv = tkv;
+    fa.layer = l;
+    fa.S = S;
+    fa.scale = 1.0f / sqrtf((float)hdt);
+    fa.out = O;
+    fa.ldo = d;
+    launch_flash_attn(fa, B, g.n_heads_t, hdt, s);
+    GemmArgs o = gemm(c->ws + w.wo, O, d, d, d);
+    o.Yf = H;
+    o.ldy = d;
+    launch_gemm_bf16(o, TF_RESID, s);
+    launch_rmsnorm_f16(H, d, c->at<float>(w.ffn_norm), g.norm_eps, d, Xn, d, M, s);
+    GemmArgs gu = gemm(c->ws + w.wgu, Xn, d, 2 * F, d);
+    gu.Yb = I;
+    gu.ldy = F;
+    launch_gemm_bf16(gu, TF_SWIGLU, s);
+    GemmArgs dn = gemm(c->ws + w.wdown, I, F, d, F);
+    dn.Yf = H;
+    dn.ldy = d;
+    launch_gemm_bf16(dn, TF_RESID, s);
+  }
+  // z = RMSNorm(h) (kept in Xn for the depth input projections), text logits
+  launch_rmsnorm_f16(H, d, c->at<float>(p.out_norm), g.norm_eps, d, Xn, d, M, s);
+  GemmArgs th = gemm(c->ws + p.text_head, Xn, d, g.vocab_text, d);
+  th.Yf = text;
+  th.ldy = g.vocab_text;
+  launch_gemm_bf16(th, TF_STORE_F32, s);
+
+  if (depth) {
+    float* U = c->at<float>(p.tf_U);
+    uint16_t* Xd = c->at<uint16_t>(p.tf_Xd);
+    uint16_t* DQ = c->at<uint16_t>(p.tf_DQ);
+    uint16_t* DK = c->at<uint16_t>(p.tf_DK);
+    uint16_t* DV = c->at<uint16_t>(p.tf_DV);
+    uint16_t* DO = c->at<uint16_t>(p.tf_DO);
+    uint16_t* DI = c->at<uint16_t>(p.tf_DI);
+    for (int j = 0; j < NQ; ++j) {
+      const DepthW& w = p.dj[j];
+      GemmArgs a = gemm(c->ws + w.in_proj, Xn, d, dd, d);
+      a.Yf = U + (long long)j * M * dd;
+      a.ldy = dd;
+      a.tok = tok + j;  // depth position j reads the true token of slot j
+      a.tok_stride = kStreams;
+      a.tok_rows = (j == 0 ? g.vocab_text : g.codebook) + 1;
+      a.emb = c->at<uint16_t>(w.emb);
+      launch_gemm_bf16(a, TF_EMB, s);
+    }
+    for (int l = 0; l < g.n_layers_d; ++l) {
+      for (int j = 0; j < NQ; ++j) {
+        const LayerW& lw = p.dj[j].layers[l];
+        float* Uj = U + (long long)j * M * dd;
+        launch_rmsnorm_f16(Uj, dd, c->at<float>(lw.attn_norm), g.norm_eps, dd, Xd, dd, M, s);
+        GemmArgs q = gemm(c->ws + lw.wqkv, Xd, dd, 3 * dd, dd);
+        q.d = dd;
+        q.hd = hdd;
+        q.S = S;
+        q.pos_const = j;
+        q.rope = c->at<float>(p.rope_d);
+        q.q = DQ + (long long)j * M * dd;
+        q.ldq = dd;
+        q.kv_paged = 0;
+        q.dk = DK + (long long)j * M * dd;
+        q.dv = DV + (long long)j * M * dd;
+        launch_gemm_bf16(q, TF_QKV, s);
+      }
+      for (int j = 0; j < NQ; ++j) {
+        const LayerW& lw = p.dj[j].layers[l];
+        float* Uj = U + (long long)j * M * dd;
+        DepthAttnArgs da{};
+        da.q = DQ;
+        da.k = DK;
+        da.v = DV;
+        da.out = DO;
+        da.M = M;
+        da.d = dd;
+        da.H = g.n_heads_d;
+        da.hd = hdd;
+        da.j = j;
+        da.scale = 1.0f / sqrtf((float)hdd);
+        launch_depth_attn(da, s);
+        GemmArgs o = gemm(c->ws + lw.wo, DO, dd, dd, dd);
+        o.Yf = Uj;
+        o.ldy = dd;
+        launch_gemm_bf16(o, TF_RESID, s);
+        launch_rmsnorm_f16(Uj, dd, c->at<float>(lw.ffn_norm), g.norm_eps, dd, Xd, dd, M, s);
+        GemmArgs gu = gemm(c->ws + lw.wgu, Xd, dd, 2 * Fd, dd);
+        gu.Yb = DI;
+        gu.ldy = Fd;
+        launch_gemm_bf16(gu, TF_SWIGLU, s);
+        GemmArgs dn = gemm(c->ws + lw.wdown, DI, Fd, dd, Fd);
+        dn.Yf = Uj;
+        dn.ldy = dd;
+        launch_gemm_bf16(dn, TF_RESID, s);
+      }
+    }
+    for (int j = 0; j < NQ; ++j) {
+      const DepthW& w = p.dj[j];
+      launch_rmsnorm_f16(U + (long long)j * M * dd, dd, c->at<float>(w.out_norm), g.norm_eps, dd, Xd, dd, M, s);
+      GemmArgs hh = gemm(c->ws + w.head, Xd, dd, g.codebook, dd);
+      hh.Yf = audio + (long long)j * g.codebook;
+      hh.ldy = (long long)NQ * g.codebook;
+      launch_gemm_bf16(hh, TF_STORE_F32, s);
+    }
+  }
+  if (want_loss) {
+    TfCeArgs ca{};
+    ca.text_logits = text;
+    ca.audio_logits = audio;
+    ca.tokens = tok;
+    ca.ce = c->at<double>(p.tf_ce);
+    ca.vocab_text = g.vocab_text;
+    ca.codebook = g.codebook;
+    launch_tf_ce(ca, M, depth, s);
+  }
+  HIPCHECK(hipGetLastError());
+}
+
 void run_step(moshi_ctx* c, int B, bool depth) {
   if (!c->use_graph) {
     enqueue_step(c, B, depth);
@@ -681,6 +883,8 @@ int moshi_create(const moshi_config* cfg, void* hip_stream, void* workspace, siz
   c->caller = (hipStream_t)hip_stream;
   const char* ng = getenv("MOSHI_NO_GRAPH");
   c->use_graph = !(ng && ng[0] == '1');
+  const char* ts = getenv("MOSHI_TF_STEPS");
+  c->tf_steps = ts && ts[0] == '1';
   int rc = guard_impl(c, [&] {
     HIPCHECK(hipGetDevice(&c->device));
     HIPCHECK(hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking));
@@ -849,8 +1053,24 @@ int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B,
       tok = c->at<int>(p.tf_tokens);
     }
     for (int b = 0; b < B; ++b) ensure_pages(c, b, S);
-    HIPCHECK(hipMemcpyAsync(c->ws + p.st_has_force, c->pin_one, 4, hipMemcpyHostToDevice, s));
     const hipMemcpyKind k = dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
+    if (p.tf_mfma && !c->tf_steps) {
+      enqueue_tf_mfma(c, tok, B, S, depth, dev ? text_logits : nullptr, dev ? audio_logits : nullptr, loss != nullptr);
+      if (!dev) {
+        if (text_logits)
+          HIPCHECK(hipMemcpyAsync(text_logits, c->ws + p.tf_text, (size_t)B * S * g.vocab_text * 4, k, s));
+        if (audio_logits && depth)
+          HIPCHECK(hipMemcpyAsync(audio_logits, c->ws + p.tf_audio, (size_t)B * S * g.n_q * g.codebook * 4, k, s));
+      }
+      if (flags & MOSHI_TF_FILL_KV) {
+        // continue streaming at frame S+1: position S, previous frame V_S
+        for (int b = 0; b < B; ++b) c->pin_in[b] = S;
+        HIPCHECK(hipMemcpyAsync(c->ws + p.st_pos, c->pin_in, B * 4, hipMemcpyHostToDevice, s));
+        HIPCHECK(hipMemcpy2DAsync(c->ws + p.st_prev, kStreams * 4, tok + (size_t)(S - 1) * kStreams,
+                                  (size_t)S * kStreams * 4, kStreams * 4, B, hipMemcpyDeviceToDevice, s));
+      }
+    } else {
+    HIPCHECK(hipMemcpyAsync(c->ws + p.st_has_force, c->pin_one, 4, hipMemcpyHostToDevice, s));
     for (int st = 0; st < S; ++st) {
       HIPCHECK(hipMemcpy2DAsync(c->ws + p.st_user, 8 * 4, tok + (size_t)st * kStreams + kSlots,
                                 (size_t)S * kStreams * 4, 8 * 4, B, hipMemcpyDeviceToDevice, s));
@@ -881,6 +1101,7 @@ int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B,
         launch_ce_rows(ca, B, depth, s);
         HIPCHECK(hipGetLastError());
       }
+    }
     }
     for (int b = 0; b < B; ++b) c->pos_h[b] = S;
     if (loss) {

@@ -1,0 +1,531 @@
+// gfx950 kernels of the teacher-forced parallel pass (bf16 models).
+//
+// Teacher forcing ([W] "训练损失" of the Moshi paper walkthrough on 139.9.1.231:
+// the model is trained on the joint sequence of eq. 6 given the true tokens)
+// turns every linear map into a dense contraction over all B*S frames, so here
+// the hot op is a matrix-core GEMM with the same fused epilogues as the
+// streaming path (RoPE + KV append, SwiGLU, residual add), plus a causal
+// flash-attention kernel on matrix cores.
+//
+// Operand precision: weights stay bf16 in HBM; the matrix cores take fp16
+// operands (v_mfma_f32_32x32x16_f16, same rate as bf16 on gfx950) with fp32
+// accumulation. Every bf16 weight value in fp16's normal range converts to
+// fp16 exactly, and activations rounded to fp16 carry 3 more mantissa bits
+// than bf16, which keeps a 32-layer pass within the parity tolerance. The
+// residual stream, softmax statistics and logits stay fp32.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "moshi_internal.h"
+
+namespace moshi {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t tf_f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float tf_bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ uint16_t tf_f2h(float f) {
+  const _Float16 h = (_Float16)f;
+  return *(const uint16_t*)&h;
+}
+__device__ __forceinline__ float tf_h2f(uint16_t v) { return (float)*(const _Float16*)&v; }
+// 8 bf16 -> 8 fp16 (exact in fp16's normal range)
+__device__ __forceinline__ u32x4t bf8_to_h8(u32x4t v) {
+  u32x4t r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    r[i] = (uint32_t)tf_f2h(__uint_as_float(w << 16)) | ((uint32_t)tf_f2h(__uint_as_float(w & 0xffff0000u)) << 16);
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// C[m][n] = sum_k X[m][k] W[n][k]  (X fp16 [M][ldx], W bf16 [N][K], K % 32 == 0)
+//
+// The matrix core computes the transposed tile W_tile * X_tile^T: A operand =
+// 32 rows of W, B operand = 32 rows of X, both read as 16-byte runs along K.
+// In the result each lane holds, for one token m, four groups of four
+// consecutive output features n -- so RoPE pairs and (gate, up) pairs sit in
+// one lane and rows are written as 8- or 16-byte runs.
+//
+// Block: 256 threads = 4 waves in a 2 (n) x 2 (m) arrangement, each wave a
+// 64 x 64 tile (2 x 2 MFMA tiles), block tile 128 (n) x 128 (m), K step 32,
+// LDS double buffer filled from registers that are loaded one step ahead.
+// Blocks are ordered in groups of 8 tiles along m so that concurrently running
+// blocks share both operand panels in L2.
+// ---------------------------------------------------------------------------
+constexpr int kTN = 128, kTM = 128, kTK = 32, kLdsRow = kTK + 8;  // padded row: 80 bytes
+
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kTN * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTM * kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = g.M, N = g.N, K = g.K;
+  // grouped rasterisation
+  const int tiles_n = (N + kTN - 1) / kTN, tiles_m = (M + kTM - 1) / kTM;
+  const int group = 8;
+  const int per_group = group * tiles_n;
+  const int gid = blockIdx.x / per_group;
+  const int first_m = gid * group;
+  const int gsize = min(tiles_m - first_m, group);
+  const int tm = first_m + (blockIdx.x % per_group) % gsize;
+  const int tn = (blockIdx.x % per_group) / gsize;
+  const int n0 = tn * kTN, m0 = tm * kTM;
+
+  // global -> register loads: 2 chunks of 8 bf16 per thread for each operand
+  u32x4t rw[2], rx[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 2, kc = (c & 3) * 8;
+      const int n = min(n0 + row, N - 1), m = min(m0 + row, M - 1);
+      rw[i] = *(const u32x4t*)(g.W + (long long)n * K + k0 + kc);
+      rx[i] = *(const u32x4t*)(g.X + (long long)m * g.ldx + k0 + kc);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c >> 2, kc = (c & 3) * 8;
+      *(u32x4t*)(&Ws[buf][row * kLdsRow + kc]) = bf8_to_h8(rw[i]);
+      *(u32x4t*)(&Xs[buf][row * kLdsRow + kc]) = rx[i];
+    }
+  };
+
+  const int wn = wave >> 1, wm = wave & 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = K / kTK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kTK);
+#pragma unroll
+    for (int ks = 0; ks < kTK / 16; ++ks) {
+      f16x8 a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wn * 64 + i * 32 + (lane & 31);
+        a[i] = *(const f16x8*)(&Ws[buf][row * kLdsRow + ks * 16 + (lane >> 5) * 8]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = wm * 64 + j * 32 + (lane & 31);
+        b[j] = *(const f16x8*)(&Xs[buf][row * kLdsRow + ks * 16 + (lane >> 5) * 8]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) {
+      lstore(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane holds token m = m0 + wm*64 + j*32 + lane%32 and features
+  // n = n0 + wn*64 + i*32 + 8*q + 4*(lane/32) + t, for q, t in 0..3
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int m = m0 + wm * 64 + j * 32 + (lane & 31);
+      if (m >= M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+        if (n >= N) continue;
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        if constexpr (EPI == TF_STORE_F32) {
+          *(float4*)(g.Yf + (long long)m * g.ldy + n) = make_float4(v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == TF_RESID) {
+          float4* p = (float4*)(g.Yf + (long long)m * g.ldy + n);
+          float4 h = *p;
+          h.x += v[0]; h.y += v[1]; h.z += v[2]; h.w += v[3];
+          *p = h;
+        } else if constexpr (EPI == TF_EMB) {
+          const int t = min(max(g.tok[(long long)m * g.tok_stride], 0), g.tok_rows - 1);
+          const uint16_t* e = g.emb + (long long)t * N + n;
+          *(float4*)(g.Yf + (long long)m * g.ldy + n) =
+              make_float4(v[0] + tf_bf2f(e[0]), v[1] + tf_bf2f(e[1]), v[2] + tf_bf2f(e[2]), v[3] + tf_bf2f(e[3]));
+        } else if constexpr (EPI == TF_SWIGLU) {
+          // (n, n+1) = (gate_i, up_i), i = n / 2
+          const float a0 = v[0] / (1.0f + expf(-v[0])) * v[1];
+          const float a1 = v[2] / (1.0f + expf(-v[2])) * v[3];
+          *(uint32_t*)(g.Yb + (long long)m * g.ldy + (n >> 1)) = (uint32_t)tf_f2h(a0) | ((uint32_t)tf_f2h(a1) << 16);
+        } else if constexpr (EPI == TF_QKV) {
+          const int part = n / g.d;  // 0 q, 1 k, 2 v
+          const int rr = n - part * g.d;
+          const int head = rr / g.hd, dim = rr - head * g.hd;
+          const int b = m / g.S, s = g.pos_const >= 0 ? g.pos_const : m - b * g.S;
+          if (part < 2) {
+#pragma unroll
+            for (int p2 = 0; p2 < 2; ++p2) {
+              const float* cs = g.rope + ((long long)s * (g.hd >> 1) + ((dim >> 1) + p2)) * 2;
+              const float x0 = v[2 * p2], x1 = v[2 * p2 + 1];
+              v[2 * p2] = x0 * cs[0] - x1 * cs[1];
+              v[2 * p2 + 1] = x0 * cs[1] + x1 * cs[0];
+            }
+          }
+          const bool to_cache = part > 0 && g.kv_paged;  // the KV cache is bf16
+          const uint32_t lo = to_cache ? ((uint32_t)tf_f2bf(v[0]) | ((uint32_t)tf_f2bf(v[1]) << 16))
+                                       : ((uint32_t)tf_f2h(v[0]) | ((uint32_t)tf_f2h(v[1]) << 16));
+          const uint32_t hi = to_cache ? ((uint32_t)tf_f2bf(v[2]) | ((uint32_t)tf_f2bf(v[3]) << 16))
+                                       : ((uint32_t)tf_f2h(v[2]) | ((uint32_t)tf_f2h(v[3]) << 16));
+          uint16_t* dst;
+          if (part == 0) {
+            dst = g.q + (long long)m * g.ldq + rr;
+          } else if (g.kv_paged) {
+            const KvView& kv = g.kv;
+            const int page = kv.page_table[b * kv.pt_stride + s / kv.pf];
+            dst = (uint16_t*)kv.base + (long long)page * kv.page_stride +
+                  ((long long)((g.layer * 2 + part - 1) * kv.n_heads + head) * kv.pf + (s % kv.pf)) * kv.hd + dim;
+          } else {
+            // flat [k|v][M][d] buffers (depth positions)
+            dst = (part == 1 ? g.dk : g.dv) + (long long)m * g.d + rr;
+          }
+          *(uint2*)dst = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
+void launch_gemm_bf16(const GemmArgs& g, int epi, hipStream_t s) {
+  const int tiles = ((g.N + kTN - 1) / kTN) * ((g.M + kTM - 1) / kTM);
+  switch (epi) {
+    case TF_STORE_F32: k_gemm_bf16<TF_STORE_F32><<<tiles, 256, 0, s>>>(g); break;
+    case TF_RESID: k_gemm_bf16<TF_RESID><<<tiles, 256, 0, s>>>(g); break;
+    case TF_EMB: k_gemm_bf16<TF_EMB><<<tiles, 256, 0, s>>>(g); break;
+    case TF_SWIGLU: k_gemm_bf16<TF_SWIGLU><<<tiles, 256, 0, s>>>(g); break;
+    case TF_QKV: k_gemm_bf16<TF_QKV><<<tiles, 256, 0, s>>>(g); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row-wise RMSNorm (float32 in) -> fp16 GEMM operand. One block per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm_f16(const float* x, long long ldx, const float* gain, float eps,
+                                                      int D, uint16_t* y, long long ldy) {
+  const long long r = blockIdx.x;
+  const float* xr = x + r * ldx;
+  __shared__ float red[4];
+  float ss = 0.f;
+  for (int k = threadIdx.x * 4; k < D; k += 1024) {
+    const float4 v = *(const float4*)(xr + k);
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float rs = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)D + eps);
+  for (int k = threadIdx.x * 4; k < D; k += 1024) {
+    const float4 v = *(const float4*)(xr + k);
+    const float4 gg = *(const float4*)(gain + k);
+    const uint32_t lo = (uint32_t)tf_f2h(v.x * rs * gg.x) | ((uint32_t)tf_f2h(v.y * rs * gg.y) << 16);
+    const uint32_t hi = (uint32_t)tf_f2h(v.z * rs * gg.z) | ((uint32_t)tf_f2h(v.w * rs * gg.w) << 16);
+    *(uint2*)(y + r * ldy + k) = make_uint2(lo, hi);
+  }
+}
+
+void launch_rmsnorm_f16(const float* x, long long ldx, const float* gain, float eps, int D, uint16_t* y,
+                         long long ldy, long long rows, hipStream_t s) {
+  k_rmsnorm_f16<<<(unsigned)rows, 256, 0, s>>>(x, ldx, gain, eps, D, y, ldy);
+}
+
+// ---------------------------------------------------------------------------
+// Teacher-forced temporal inputs: row m = (b, s) sums the embeddings of
+// V_{s-1} (s = 0: the all-pad initial frame). tokens [B][S][17].
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tf_embed(EmbedArgs a, const int* tokens, int S, int pad_text, int pad_audio) {
+  const long long m = blockIdx.x;
+  const int b = (int)(m / S), s = (int)(m - (long long)b * S);
+  const int i = blockIdx.y * 256 + threadIdx.x;
+  int t[kStreams];
+#pragma unroll
+  for (int k = 0; k < kStreams; ++k)
+    t[k] = s == 0 ? (k == 0 ? pad_text : pad_audio) : tokens[((long long)b * S + s - 1) * kStreams + k];
+  if (i >= a.d) return;
+  float v[kStreams];
+#pragma unroll
+  for (int k = 0; k < kStreams; ++k) {
+    const int tk = min(max(t[k], 0), a.rows[k] - 1);
+    v[k] = tf_bf2f(((const uint16_t*)a.table)[(a.row0[k] + tk) * (long long)a.d + i]);
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kStreams; ++k) acc += v[k];
+  a.h[m * a.d + i] = acc;
+}
+
+void launch_tf_embed(const EmbedArgs& a, const int* tokens, long long M, int S, int pad_text, int pad_audio,
+                     hipStream_t s) {
+  dim3 grid((unsigned)M, (a.d + 255) / 256);
+  k_tf_embed<<<grid, 256, 0, s>>>(a, tokens, S, pad_text, pad_audio);
+}
+
+// ---------------------------------------------------------------------------
+// Causal flash attention over the paged cache (hd = 128, bf16). Block = 4 waves
+// = 128 queries of one (b, head); wave w owns queries q0 + 32w .. +31. Key
+// tiles of 64 are staged in LDS (K as rows, V transposed); per tile each wave
+// computes S = Q K^T with 16 MFMAs (Q fragments stay in registers), applies
+// the causal mask and an online softmax per query row (row statistics reduced
+// across the 32 lanes that hold a row's keys), writes P as bf16 to LDS and
+// accumulates O += P V with 16 more MFMAs. Key tiles above the diagonal are
+// skipped.
+// ---------------------------------------------------------------------------
+constexpr int kFaKT = 64, kFaQT = 128;
+constexpr int kFaVRow = kFaKT + 8;   // V^T tile row
+constexpr int kFaPRow = kFaKT + 8;   // P tile row
+
+template <int kFaHD>
+__global__ __launch_bounds__(256) void k_flash_attn(FlashArgs f) {
+  constexpr int kFaKRow = kFaHD + 8;  // K tile row (bf16), padded
+  constexpr int CPR = kFaHD / 8;      // 16-byte chunks per K/V row
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFaKT * kFaKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kFaHD * kFaVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kFaQT * kFaPRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = f.S;
+  const int q0 = qt * kFaQT;
+  const int qw = q0 + wave * 32;
+  const KvView& kv = f.kv;
+  const long long head_off = (long long)((f.layer * 2) * kv.n_heads + h) * kv.pf * kv.hd;
+  const long long v_off = (long long)kv.n_heads * kv.pf * kv.hd;
+
+  // Q fragments: lane holds Q[qw + lane%32][16*ks + 8*(lane/32) .. +7]
+  f16x8 qf[kFaHD / 16];
+  {
+    const int qrow = min(qw + (lane & 31), S - 1);
+    const uint16_t* qp = f.q + ((long long)b * S + qrow) * f.ldq + h * kFaHD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < kFaHD / 16; ++ks) qf[ks] = *(const f16x8*)(qp + 16 * ks);
+  }
+  f32x16 o[kFaHD / 32];
+#pragma unroll
+  for (int t = 0; t < kFaHD / 32; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float mrow[16], lrow[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+  const float scale = f.scale;
+  const int kend = min(q0 + kFaQT, S);  // keys needed by this query tile
+  for (int k0 = 0; k0 < kend; k0 += kFaKT) {
+    // stage K and V^T of keys k0 .. k0+63 (clamped to S-1)
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kFaKT * CPR / 256; ++i) {
+      const int c = tid + 256 * i;
+      const int kr = c / CPR, hc = (c % CPR) * 8;
+      const int key = min(k0 + kr, S - 1);
+      const int page = kv.page_table[b * kv.pt_stride + key / kv.pf];
+      const uint16_t* kp = (const uint16_t*)kv.base + (long long)page * kv.page_stride + head_off +
+                           (long long)(key % kv.pf) * kv.hd + hc;
+      const u32x4t kk = bf8_to_h8(*(const u32x4t*)kp);
+      const u32x4t vv = bf8_to_h8(*(const u32x4t*)(kp + v_off));
+      *(u32x4t*)(&Ks[kr * kFaKRow + hc]) = kk;
+      const uint16_t* ve = (const uint16_t*)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(hc + e) * kFaVRow + kr] = ve[e];
+    }
+    __syncthreads();
+    if (k0 > qw + 31) continue;  // whole tile above this wave's diagonal
+    // S = Q K^T for keys k0 + 32t + lane%32
+    f32x16 sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < kFaHD / 16; ++ks) {
+        const f16x8 kf = *(const f16x8*)(&Ks[(32 * t + (lane & 31)) * kFaKRow + 16 * ks + 8 * (lane >> 5)]);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[ks], kf, sc[t], 0, 0, 0);
+      }
+    }
+    // C layout: sc[t][r] = S[query qw + 8*(r/4) + 4*(lane/32) + r%4][key k0 + 32t + lane%32]
+    float alpha[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qrow = qw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int key = k0 + 32 * t + (lane & 31);
+        float v = sc[t][r] * scale;
+        v = (key <= qrow && key < S) ? v : -INFINITY;
+        sc[t][r] = v;
+        mx = fmaxf(mx, v);
+      }
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      const float mn = fmaxf(mrow[r], mx);
+      alpha[r] = mn == -INFINITY ? 1.f : expf(mrow[r] - mn);
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float pv = mn == -INFINITY ? 0.f : expf(sc[t][r] - mn);
+        sc[t][r] = pv;
+        sum += pv;
+      }
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+      lrow[r] = lrow[r] * alpha[r] + sum;
+      mrow[r] = mn;
+    }
+    // P (bf16) to LDS rows of this wave: P[q - q0][key - k0]
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ql = wave * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        Ps[ql * kFaPRow + 32 * t + (lane & 31)] = tf_f2h(sc[t][r]);
+      }
+#pragma unroll
+    for (int t = 0; t < kFaHD / 32; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha[r];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P stores done before the wave reads them
+    __builtin_amdgcn_wave_barrier();
+    // O += P V: A = P[q][16ks + 8*(lane/32) ..], B = V[16ks + 8*(lane/32) + i][32t + lane%32]
+#pragma unroll
+    for (int ks = 0; ks < kFaKT / 16; ++ks) {
+      const f16x8 pf = *(const f16x8*)(&Ps[(wave * 32 + (lane & 31)) * kFaPRow + 16 * ks + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int t = 0; t < kFaHD / 32; ++t) {
+        const f16x8 vf = *(const f16x8*)(&Vt[(32 * t + (lane & 31)) * kFaVRow + 16 * ks + 8 * (lane >> 5)]);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf, vf, o[t], 0, 0, 0);
+      }
+    }
+  }
+  // O / l -> bf16 out[b*S + q][h*hd + 32t + lane%32]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int qrow = qw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (qrow >= S) continue;
+    const float inv = 1.f / lrow[r];
+    uint16_t* op = f.out + ((long long)b * S + qrow) * f.ldo + h * kFaHD + (lane & 31);
+#pragma unroll
+    for (int t = 0; t < kFaHD / 32; ++t) op[32 * t] = tf_f2h(o[t][r] * inv);
+  }
+}
+
+void launch_flash_attn(const FlashArgs& f, int B, int H, int hd, hipStream_t s) {
+  dim3 grid((f.S + kFaQT - 1) / kFaQT, H, B);
+  if (hd == 64)
+    k_flash_attn<64><<<grid, 256, 0, s>>>(f);
+  else
+    k_flash_attn<128><<<grid, 256, 0, s>>>(f);
+}
+
+// ---------------------------------------------------------------------------
+// Depth attention of the teacher-forced pass: frame m, depth position j, head
+// h attends to positions 0..j of the same frame (at most 8). One wave per
+// (m, head); q, k, v are bf16 [position][M][d] buffers.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_depth_attn(DepthAttnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long item = (long long)blockIdx.x * 4 + wave;  // (m, head)
+  const long long m = item / a.H;
+  const int h = (int)(item - m * a.H);
+  if (m >= a.M) return;
+  const int hd = a.hd;  // 64: one element per lane
+  const int j = a.j;
+  const float qv = lane < hd ? tf_h2f(a.q[((long long)j * a.M + m) * a.d + h * hd + lane]) : 0.f;
+  float sc[8];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (p > j) break;
+    float v = lane < hd ? qv * tf_h2f(a.k[((long long)p * a.M + m) * a.d + h * hd + lane]) : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    sc[p] = v * a.scale;
+    mx = fmaxf(mx, sc[p]);
+  }
+  float l = 0.f, o = 0.f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (p > j) break;
+    const float w = expf(sc[p] - mx);
+    l += w;
+    if (lane < hd) o = fmaf(w, tf_h2f(a.v[((long long)p * a.M + m) * a.d + h * hd + lane]), o);
+  }
+  if (lane < hd) a.out[m * a.d + h * hd + lane] = tf_f2h(o / l);
+}
+
+void launch_depth_attn(const DepthAttnArgs& a, hipStream_t s) {
+  const long long items = (long long)a.M * a.H;
+  k_depth_attn<<<(unsigned)((items + 3) / 4), 256, 0, s>>>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-entropy rows of the teacher-forced pass: ce[m*9 + slot] =
+// logsumexp(l) - l[target] or -1 for a pad target. Grid (M, 9).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tf_ce(TfCeArgs a) {
+  const long long m = blockIdx.x;
+  const int slot = blockIdx.y, tid = threadIdx.x;
+  const int n = slot == 0 ? a.vocab_text : a.codebook;
+  const float* l = slot == 0 ? a.text_logits + m * a.vocab_text
+                             : a.audio_logits + (m * 8 + (slot - 1)) * (long long)a.codebook;
+  const int t = a.tokens[m * kStreams + slot];
+  const int pad = n;
+  double* out = a.ce + m * kSlots + slot;
+  if (t < 0 || t >= pad) {
+    if (tid == 0) *out = -1.0;
+    return;
+  }
+  __shared__ float s_f[256];
+  __shared__ double s_d[256];
+  float mx = -INFINITY;
+  for (int i = tid; i < n; i += 256) mx = fmaxf(mx, l[i]);
+  s_f[tid] = mx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s_f[tid] = fmaxf(s_f[tid], s_f[tid + o]);
+    __syncthreads();
+  }
+  mx = s_f[0];
+  double sum = 0.0;
+  for (int i = tid; i < n; i += 256) sum += (double)expf(l[i] - mx);
+  s_d[tid] = sum;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) s_d[tid] += s_d[tid + o];
+    __syncthreads();
+  }
+  if (tid == 0) *out = log(s_d[0]) + (double)mx - (double)l[t];
+}
+
+void launch_tf_ce(const TfCeArgs& a, long long M, bool with_audio, hipStream_t s) {
+  dim3 grid((unsigned)M, with_audio ? kSlots : 1);
+  k_tf_ce<<<grid, 256, 0, s>>>(a);
+}
+
+}  // namespace moshi

@@ -117,6 +117,63 @@ struct CeRowsArgs {
   int S, s;
 };
 
+enum TfEpi { TF_STORE_F32 = 0, TF_RESID = 1, TF_EMB = 2, TF_SWIGLU = 3, TF_QKV = 4 };
+
+struct GemmArgs {
+  const uint16_t* W;  // [N][K] bf16
+  const uint16_t* X;  // [M][ldx] bf16
+  long long ldx;
+  int M, N, K;
+  float* Yf;          // float32 output / residual stream [M][ldy]
+  uint16_t* Yb;       // bf16 output [M][ldy] (SwiGLU)
+  long long ldy;
+  // TF_EMB: Yf = acc + emb[tok[m * tok_stride]]
+  const int* tok;
+  long long tok_stride;
+  int tok_rows;
+  const uint16_t* emb;
+  // TF_QKV
+  int d, hd, S;
+  int pos_const;      // >= 0: every row at this RoPE position (depth); < 0: position = m % S
+  const float* rope;
+  uint16_t* q;        // [M][ldq]
+  long long ldq;
+  KvView kv;
+  int kv_paged;
+  int layer;
+  uint16_t* dk;       // flat K/V outputs [M][d] when !kv_paged
+  uint16_t* dv;
+};
+
+struct FlashArgs {
+  const uint16_t* q;  // [B*S][ldq]
+  long long ldq;
+  KvView kv;
+  int layer;
+  int S;
+  float scale;
+  uint16_t* out;      // [B*S][ldo]
+  long long ldo;
+};
+
+struct DepthAttnArgs {
+  const uint16_t* q;  // [8][M][d]
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;      // [M][d]
+  long long M;
+  int d, H, hd, j;
+  float scale;
+};
+
+struct TfCeArgs {
+  const float* text_logits;   // [M][vocab_text]
+  const float* audio_logits;  // [M][8][codebook]
+  const int* tokens;          // [M][17] targets V_s
+  double* ce;                 // [M][9]
+  int vocab_text, codebook;
+};
+
 // launchers (kernels_decode.hip)
 void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s);
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s);
@@ -129,5 +186,14 @@ void launch_convert(const float* src, long long rows, int cols, void* dst, bool 
 void launch_ce_rows(const CeRowsArgs& a, int B, bool with_audio, hipStream_t s);
 void launch_ce_reduce(const double* ce, long long n_rows, int n_slots, double* res, hipStream_t s);
 void launch_rope_table(float* out, int P, int hd, double base, hipStream_t s);
+// launchers (kernels_tf.hip)
+void launch_gemm_bf16(const GemmArgs& g, int epi, hipStream_t s);
+void launch_rmsnorm_f16(const float* x, long long ldx, const float* gain, float eps, int D, uint16_t* y,
+                         long long ldy, long long rows, hipStream_t s);
+void launch_tf_embed(const EmbedArgs& a, const int* tokens, long long M, int S, int pad_text, int pad_audio,
+                     hipStream_t s);
+void launch_flash_attn(const FlashArgs& f, int B, int H, int hd, hipStream_t s);
+void launch_depth_attn(const DepthAttnArgs& a, hipStream_t s);
+void launch_tf_ce(const TfCeArgs& a, long long M, bool with_audio, hipStream_t s);
 
 }  // namespace moshi

@@ -75,3 +75,35 @@ def test_mid_teacher_forced_logits_and_loss():
     ref = cross_entropy_loss(cfg, V, rt, ra)
     for k in ("ce_text", "ce_audio", "ce_total"):
         assert loss[k] == pytest.approx(ref[k], rel=1e-3)
+
+
+def test_mid_bf16_teacher_forced_long_ragged():
+    """Matrix-core teacher-forced pass over 2 x 300 frames (several 128-frame
+    query tiles and 64-key tiles with a ragged tail), logits and loss against the
+    oracle; then continue streaming after a FILL_KV pass."""
+    from full_duplex_speech_amd import Moshi
+    from oracle import cross_entropy_loss
+    cfg = config("mid_bf16")
+    w = generate_weights(cfg, seed=0)
+    B, S = 2, 300
+    V = np.stack([prompt_V(cfg, b, S) for b in range(B)])
+    model = Oracle(cfg, w)
+    eng = Moshi(cfg, max_batch=B)
+    eng.load_weights(w)
+    lt, la, loss = eng.forward_teacher_forced(V)
+    refs = [model.forward_teacher_forced(V[b])[:2] for b in range(B)]
+    rt = np.stack([r[0] for r in refs])
+    ra = np.stack([r[1] for r in refs])
+    worst = max(rel_l2(lt[b, s], rt[b, s]) for b in range(B) for s in range(S))
+    worst = max(worst, max(rel_l2(la[b, s, j], ra[b, s, j]) for b in range(B) for s in range(0, S, 7) for j in range(8)))
+    print(f"mid_bf16 teacher-forced 2x300: worst rel-L2 {worst:.2e}")
+    assert worst <= 1e-2
+    # argmax parity where the oracle's margin is clear
+    from oracle import top2_margin
+    mt = top2_margin(rt)
+    ok = mt > 0.05
+    assert (np.argmax(lt, -1)[ok] == np.argmax(rt, -1)[ok]).all()
+    ref = cross_entropy_loss(cfg, V, rt, ra)
+    for k in ("ce_text", "ce_audio", "ce_total"):
+        assert loss[k] == pytest.approx(ref[k], rel=1e-3)
+    eng.close()
