@@ -611,6 +611,237 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
   unit(pair, g, pair, g, false);
 }
 
+// ---------------------------------------------------------------------------
+// Batched weight-streaming GEMV on matrix cores (2..16 conversations, bf16
+// weights). v_mfma_f32_16x16x32_f16 computes a 16 (rows of W) x 16 (tokens)
+// tile: lane l supplies W[row0 + l%16][k0 + 8*(l/16) .. +7] (a 16-byte load)
+// and the fp16 normalised input of token l%16 at the same k, and receives
+// rows row0 + 4*(l/16) + 0..3 of token l%16 -- so RoPE and SwiGLU pairs stay
+// in one lane. Tokens past the batch read zeros. Units are (16-row group,
+// K-group of 8 such loads); as in the single-vector kernel each lane refills
+// its weight registers with the next unit's data right after use. The
+// conversion of a bf16 weight to fp16 is exact in fp16's normal range.
+// ---------------------------------------------------------------------------
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t h2pack(float a, float b) {
+  const _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)(*(const uint16_t*)&x) | ((uint32_t)(*(const uint16_t*)&y) << 16);
+}
+__device__ __forceinline__ h16x8 bf8_to_h16x8(u32x4 v) {
+  u32x4 r;
+  r.x = h2pack(bf_lo(v.x), bf_hi(v.x));
+  r.y = h2pack(bf_lo(v.y), bf_hi(v.y));
+  r.z = h2pack(bf_lo(v.z), bf_hi(v.z));
+  r.w = h2pack(bf_lo(v.w), bf_hi(v.w));
+  return *(const h16x8*)&r;
+}
+
+constexpr int kMfmaLPG = 8;  // 32-wide K chunks per unit
+
+template <int EPI>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int B, int k_begin, int k_end, int SK) {
+  constexpr int GROUP = 32 * kMfmaLPG;
+  extern __shared__ uint16_t xh[];  // fp16 [B][KP], zero past the chunk
+  __shared__ float s_red[kStreamWaves][16];
+  __shared__ float s_rstd[16];
+  __shared__ f32x4v s_part[kStreamWaves][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+  const int KC = k_end - k_begin;  // columns handled by this launch
+  const int ng = (KC + GROUP - 1) / GROUP;
+  const int KP = ng * GROUP;
+  const int ngroups = (N + 15) / 16;
+  // block = (8 / SK) row groups x SK slices of K; a wave walks its slice
+  const int RG = kStreamWaves / SK;
+  const int rgl = wave / SK, ks = wave - rgl * SK;
+  const int g_lo = ks * ng / SK, g_hi = (ks + 1) * ng / SK;  // this wave's K-groups
+  const int nsets = (ngroups + RG - 1) / RG;
+  const int my_sets = blockIdx.x < nsets ? (nsets - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int per_set = g_hi - g_lo;
+  const int units = my_sets * per_set;
+  const uint16_t* Wb = (const uint16_t*)a.W;
+  const int tok = lane & 15, quad = lane >> 4;
+
+  // per-token epilogue constants (this lane's token)
+  const int tk = min(tok, B - 1);
+  int pos_t = 0, page_t = 0, emb_t = 0;
+  if constexpr (EPI == EPI_QKV) {
+    pos_t = a.pos ? a.pos[tk] : a.pos_const;
+    page_t = a.kv.page_table ? a.kv.page_table[tk * a.kv.pt_stride + pos_t / a.kv.pf] : tk;
+  }
+  if constexpr (EPI == EPI_EMB) emb_t = min(max(a.tok[tk * a.tok_stride + a.tok_col], 0), a.tok_rows - 1);
+
+  auto grp_of = [&](int set) { return min((blockIdx.x + set * (int)gridDim.x) * RG + rgl, ngroups - 1); };
+  u32x4 w[kMfmaLPG];
+  auto load_slot = [&](int grp, int g, int i) {
+    const int row = min(grp * 16 + tok, N - 1);
+    const int k = min(k_begin + g * GROUP + i * 32 + quad * 8, K - 8);
+    w[i] = __builtin_nontemporal_load((const u32x4*)(Wb + (long long)row * K + k));
+  };
+  if (units > 0) {
+#pragma unroll
+    for (int i = 0; i < kMfmaLPG; ++i) load_slot(grp_of(0), g_lo, i);
+  }
+
+  // prologue: RMSNorm statistics over the full K, fp16 inputs of [k_begin, k_end) in LDS
+  if (a.gain) {
+    float rs[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) rs[b] = 0.f;
+    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        if (b < B) {
+          const float4 v = *(const float4*)(a.x + (long long)b * a.ldx + k);
+          rs[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      rs[b] = wave_sum(rs[b]);
+      if (lane == 0) s_red[wave][b] = rs[b];
+    }
+    __syncthreads();
+    if (tid < 16) {
+      float t = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kStreamWaves; ++w2) t += s_red[w2][tid];
+      s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+  for (int i = tid * 4; i < B * KP; i += 64 * kStreamWaves * 4) {
+    const int b = i / KP, k = i - b * KP;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < KC) {
+      v = *(const float4*)(a.x + (long long)b * a.ldx + k_begin + k);
+      if (a.gain) {
+        const float r = s_rstd[b];
+        const float4 g = *(const float4*)(a.gain + k_begin + k);
+        v.x *= r * g.x; v.y *= r * g.y; v.z *= r * g.z; v.w *= r * g.w;
+      }
+    }
+    *(uint2*)(xh + i) = make_uint2(h2pack(v.x, v.y), h2pack(v.z, v.w));
+  }
+  __syncthreads();
+  if (my_sets == 0) return;
+
+  // epilogue operands of a row group (residual / embedding values, RoPE
+  // angles), loaded one set ahead and carried
+  auto load_pre = [&](int grp, float (&pre)[4]) {
+    const int r0 = min(grp * 16 + quad * 4, N - 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pre[r] = 0.f;
+    if constexpr (EPI == EPI_RESID) {
+      const float4 v = *(const float4*)(a.y + (long long)tk * a.ldy + r0);
+      pre[0] = v.x; pre[1] = v.y; pre[2] = v.z; pre[3] = v.w;
+    }
+    if constexpr (EPI == EPI_EMB) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pre[r] = bf2f(((const uint16_t*)a.emb)[(long long)emb_t * N + r0 + r]);
+    }
+    if constexpr (EPI == EPI_QKV) {
+      const int dim = (r0 % a.d) % a.hd;
+      const float* cs = a.rope + ((long long)pos_t * (a.hd >> 1) + (dim >> 1)) * 2;
+      pre[0] = cs[0]; pre[1] = cs[1]; pre[2] = cs[2]; pre[3] = cs[3];
+    }
+  };
+  float pre[4], pre_n[4];
+  load_pre(grp_of(0), pre);
+  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* xrow = xh + (long long)tk * KP;
+  const bool tok_live = tok < B;
+
+  // units (set, K-group) in order; the steady-state loop always refills, the
+  // last unit is peeled so that no load sits behind a data-dependent branch
+  auto unit = [&](int set, int g, bool refill) {
+    const int grp = grp_of(set);
+    int nset = set, ngk = g + 1;
+    if (ngk == g_hi) {
+      ngk = g_lo;
+      ++nset;
+    }
+    const int ngrp = grp_of(nset);
+    if (refill) load_pre(ngrp, pre_n);
+#pragma unroll
+    for (int i = 0; i < kMfmaLPG; ++i) {
+      const int k = g * GROUP + i * 32 + quad * 8;
+      u32x4 xv = *(const u32x4*)(xrow + k);
+      if (!tok_live) xv = u32x4{0, 0, 0, 0};
+      const h16x8 af = bf8_to_h16x8(w[i]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, *(const h16x8*)&xv, acc, 0, 0, 0);
+      if (refill) load_slot(ngrp, ngk, i);
+      // keep slot order: converting a later slot early would wait for its load
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g == g_hi - 1) {
+      // reduce the SK slices of each row group through LDS (fixed order)
+      if (SK > 1) {
+        s_part[wave][lane] = acc;
+        __syncthreads();
+        if (ks == 0) {
+          for (int j = 1; j < SK; ++j) {
+            const f32x4v t = s_part[wave + j][lane];
+            acc[0] += t[0]; acc[1] += t[1]; acc[2] += t[2]; acc[3] += t[3];
+          }
+        }
+        __syncthreads();
+      }
+      const int row = grp * 16 + quad * 4;
+      const bool own = (blockIdx.x + set * (int)gridDim.x) * RG + rgl < ngroups;
+      if (ks == 0 && tok_live && own && row < N) {
+        float* y = a.y + (long long)tok * a.ldy;
+        const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
+        if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
+          *(float4*)(y + row) = make_float4(v0 + pre[0], v1 + pre[1], v2 + pre[2], v3 + pre[3]);
+        } else if constexpr (EPI == EPI_SWIGLU) {
+          *(float2*)(y + (row >> 1)) = make_float2(v0 / (1.0f + expf(-v0)) * v1, v2 / (1.0f + expf(-v2)) * v3);
+        } else if constexpr (EPI == EPI_QKV) {
+          const int part = row / a.d;
+          const int rr = row - part * a.d;
+          const int head = rr / a.hd, dim = rr - head * a.hd;
+          float x0 = v0, x1 = v1, x2 = v2, x3 = v3;
+          if (part < 2) {
+            x0 = v0 * pre[0] - v1 * pre[1];
+            x1 = v0 * pre[1] + v1 * pre[0];
+            x2 = v2 * pre[2] - v3 * pre[3];
+            x3 = v2 * pre[3] + v3 * pre[2];
+          }
+          if (part == 0) {
+            *(float4*)(y + rr) = make_float4(x0, x1, x2, x3);
+          } else {
+            const long long off = (long long)page_t * a.kv.page_stride +
+                                  ((long long)((a.layer * 2 + part - 1) * a.kv.n_heads + head) * a.kv.pf +
+                                   (pos_t % a.kv.pf)) * a.kv.hd + dim;
+            if (a.kv_bf16) {
+              const uint32_t lo = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
+              const uint32_t hi = (uint32_t)f2bf(x2) | ((uint32_t)f2bf(x3) << 16);
+              *(uint2*)((uint16_t*)a.kv.base + off) = make_uint2(lo, hi);
+            } else {
+              *(float4*)((float*)a.kv.base + off) = make_float4(x0, x1, x2, x3);
+            }
+          }
+        }
+      }
+      acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pre[r] = pre_n[r];
+    }
+  };
+  int set = 0, g = g_lo;
+  for (int u = 0; u < units - 1; ++u) {
+    unit(set, g, true);
+    if (++g == g_hi) {
+      g = g_lo;
+      ++set;
+    }
+  }
+  unit(set, g, false);
+}
+
 static int device_cus() {
   static int cus = 0;
   if (!cus) {
@@ -677,7 +908,52 @@ static void gemv_dispatch(const GemvArgs& a, int B, int epi, hipStream_t s) {
   }
 }
 
+template <int EPI>
+static void gemv_mfma_launch(const GemvArgs& a, int B, hipStream_t s) {
+  constexpr int GROUP = 32 * kMfmaLPG;
+  const int ngroups = (a.N + 15) / 16;
+  // split K inside a block until the grid has about 2048 waves
+  int SK = 1;
+  const int ng_launch = (std::min(a.K, (65536 / (2 * B)) / GROUP * GROUP) + GROUP - 1) / GROUP;
+  while (SK < kStreamWaves && ngroups * SK < 2048 && SK * 2 <= ng_launch) SK *= 2;
+  const int RG = kStreamWaves / SK;
+  const int nsets = (ngroups + RG - 1) / RG;
+  dim3 grid(std::min(nsets, 2 * device_cus()));
+  const int T = 64 * kStreamWaves;
+  // the fp16 inputs of one launch must fit in 64 KB of LDS: long rows (the
+  // residual down projection) run as several launches over K ranges, each
+  // adding its partial product into y
+  const int cap = (65536 / (2 * B)) / GROUP * GROUP;
+  if (a.K <= cap || EPI != EPI_RESID) {
+    const int KP = (a.K + GROUP - 1) / GROUP * GROUP;
+    k_gemv_mfma<EPI><<<grid, T, (size_t)B * KP * 2, s>>>(a, B, 0, a.K, SK);
+    return;
+  }
+  const int passes = (a.K + cap - 1) / cap;
+  const int step = ((a.K + passes - 1) / passes + 7) / 8 * 8;
+  for (int k0 = 0; k0 < a.K; k0 += step) {
+    const int k1 = std::min(a.K, k0 + step);
+    const int KP = (k1 - k0 + GROUP - 1) / GROUP * GROUP;
+    k_gemv_mfma<EPI><<<grid, T, (size_t)B * KP * 2, s>>>(a, B, k0, k1, SK);
+  }
+}
+
 void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s) {
+  // batched bf16: matrix cores, when the fp16 inputs fit in LDS
+  if (bf16 && B >= 2 && B <= 16 && (size_t)B * ((a.K + 255) / 256 * 256) * 2 <= 65536 * 3 && a.K % 8 == 0 &&
+      a.N % 4 == 0) {
+    const int cap = (65536 / (2 * B)) / 256 * 256;
+    if (a.K <= cap || epi == EPI_RESID) {
+      switch (epi) {
+        case EPI_STORE: gemv_mfma_launch<EPI_STORE>(a, B, s); break;
+        case EPI_RESID: gemv_mfma_launch<EPI_RESID>(a, B, s); break;
+        case EPI_EMB: gemv_mfma_launch<EPI_EMB>(a, B, s); break;
+        case EPI_SWIGLU: gemv_mfma_launch<EPI_SWIGLU>(a, B, s); break;
+        case EPI_QKV: gemv_mfma_launch<EPI_QKV>(a, B, s); break;
+      }
+      return;
+    }
+  }
   if (bf16)
     gemv_dispatch<true>(a, B, epi, s);
   else
