@@ -915,7 +915,8 @@ static void gemv_mfma_launch(const GemvArgs& a, int B, hipStream_t s) {
   // split K inside a block until the grid has about 2048 waves
   int SK = 1;
   const int ng_launch = (std::min(a.K, (65536 / (2 * B)) / GROUP * GROUP) + GROUP - 1) / GROUP;
-  while (SK < kStreamWaves && ngroups * SK < 2048 && SK * 2 <= ng_launch) SK *= 2;
+  // finest sets (one row group per block) balance the per-CU byte counts best
+  while (SK < kStreamWaves && SK * 2 <= ng_launch) SK *= 2;
   const int RG = kStreamWaves / SK;
   const int nsets = (ngroups + RG - 1) / RG;
   dim3 grid(std::min(nsets, 2 * device_cus()));
