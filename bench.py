@@ -22,6 +22,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "gemv_gate_up_b1_7b_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "full_duplex_speech_amd", "csrc", "kernels_decode.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs, or None once the kernel source has changed."""
+    import hashlib
+    try:
+        fields = dict(l.split(": ", 1) for l in open(COUNTERS).read().splitlines() if ": " in l and not l.startswith("|"))
+        if fields.get("kernel_source_sha256", "").strip() != hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -71,6 +86,8 @@ def main():
     ap.add_argument("--config", default="b1_7b")
     ap.add_argument("--cpu-frames", type=int, default=None, help="oracle frames timed on the host (0: skip)")
     ap.add_argument("--kernel-iters", type=int, default=320)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the frame step runs on a "
@@ -163,8 +180,9 @@ def main():
     if not tf_mode:
         us, nbytes = fds.moshi_time_kernel(ctx, "ffn_gate_up", B, args.kernel_iters)
         ach = nbytes / (us * 1e-6) / 1e9
+        traffic = measured_traffic() if (cfg.name == "b1_7b" and B == 1) else None
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "k_gemv (RMSNorm + gate/up + SiLU product, one temporal layer)",
                     "bytes_per_launch": nbytes, "us_per_launch": round(us, 3)}
         others = {}
@@ -181,6 +199,15 @@ def main():
         frame_bytes = lin * esz + kv
         roofline["frame_bytes_per_step"] = frame_bytes
         roofline["frame_frac"] = round(frame_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    if args.calibrate_copy:
+        # an elementwise kernel that reads 256 MiB and writes 256 MiB
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration: elementwise add over {src.numel() * 4 / 2**20:.0f} MiB (read + write), 3 times")
 
     cpu = None
     if cpu_frames:
