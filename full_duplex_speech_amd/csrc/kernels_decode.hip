@@ -380,6 +380,43 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_stream(GemvArgs a) {
   gemv_epilogue<NB, BF, EPI, 2>(a, row0, 2, acc);
 }
 
+// Outputs of one row pair (rows row, row + 1) of one input vector, given the
+// two dot products s0, s1 and the pair's epilogue operands p0, p1 (residual,
+// embedding row, or RoPE cos/sin).
+template <int EPI>
+__device__ __forceinline__ void pair_store(const GemvArgs& a, float* y, int row, float s0, float s1, float p0,
+                                           float p1, int pos, int page) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
+    y[row] = s0 + p0;
+    if (row + 1 < a.N) y[row + 1] = s1 + p1;
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    y[row >> 1] = s0 / (1.0f + expf(-s0)) * s1;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int part = row / a.d;
+    const int rr = row - part * a.d;
+    const int head = rr / a.hd, dim = rr - head * a.hd;
+    float x0 = s0, x1 = s1;
+    if (part < 2) {
+      x0 = s0 * p0 - s1 * p1;
+      x1 = s0 * p1 + s1 * p0;
+    }
+    if (part == 0) {
+      y[rr] = x0;
+      y[rr + 1] = x1;
+    } else {
+      const long long off = (long long)page * a.kv.page_stride +
+                            ((long long)((a.layer * 2 + part - 1) * a.kv.n_heads + head) * a.kv.pf +
+                             (pos % a.kv.pf)) * a.kv.hd + dim;
+      if (a.kv_bf16) {
+        const uint32_t v = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
+        *(uint32_t*)((uint16_t*)a.kv.base + off) = v;
+      } else {
+        *(float2*)((float*)a.kv.base + off) = make_float2(x0, x1);
+      }
+    }
+  }
+}
+
 // Persistent variant of the streaming GEMV: a grid of about two blocks per CU;
 // every wave walks a sequence of units (row pair, K-group of LPG wave-wide
 // loads per row) assigned round-robin over all waves. The weight registers of
@@ -553,36 +590,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
             s0 = acc[0][bb]; s1 = acc[1][bb]; p0 = pre[0][bb]; p1 = pre[1][bb];
             pos = pos_b[bb]; page = page_b[bb];
           }
-        float* y = a.y + (long long)b * a.ldy;
-        if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
-          y[row] = s0 + p0;
-          if (row + 1 < N) y[row + 1] = s1 + p1;
-        } else if constexpr (EPI == EPI_SWIGLU) {
-          y[row >> 1] = s0 / (1.0f + expf(-s0)) * s1;
-        } else if constexpr (EPI == EPI_QKV) {
-          const int part = row / a.d;
-          const int rr = row - part * a.d;
-          const int head = rr / a.hd, dim = rr - head * a.hd;
-          float x0 = s0, x1 = s1;
-          if (part < 2) {
-            x0 = s0 * p0 - s1 * p1;
-            x1 = s0 * p1 + s1 * p0;
-          }
-          if (part == 0) {
-            y[rr] = x0;
-            y[rr + 1] = x1;
-          } else {
-            const long long off = (long long)page * a.kv.page_stride +
-                                  ((long long)((a.layer * 2 + part - 1) * a.kv.n_heads + head) * a.kv.pf +
-                                   (pos % a.kv.pf)) * a.kv.hd + dim;
-            if (a.kv_bf16) {
-              const uint32_t v = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
-              *(uint32_t*)((uint16_t*)a.kv.base + off) = v;
-            } else {
-              *(float2*)((float*)a.kv.base + off) = make_float2(x0, x1);
-            }
-          }
-        }
+        pair_store<EPI>(a, a.y + (long long)b * a.ldy, row, s0, s1, p0, p1, pos, page);
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -609,6 +617,127 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
     g = ngrp;
   }
   unit(pair, g, pair, g, false);
+}
+
+
+// Split-K variant for one input vector and matrices with fewer row pairs than
+// the chip has waves (the depth model's 1024-row maps, the depth heads): a
+// block holds RG = 8/SK row pairs with SK waves each; wave s of a pair takes
+// the K spans s, s+SK, s+2SK, ... (at most SPW of them, every lane one
+// 16-byte load per row and span), so each block streams only a few KB and all
+// CUs share the matrix. All weight loads are issued before the RMSNorm
+// prologue; spans past K read clamped addresses against zero-padded inputs.
+// The SK partial sums meet in LDS and are added in wave order.
+template <bool BF, int EPI, int SPW>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, int SK) {
+  constexpr int EPL = WLoad<BF>::EPL, SPAN = 64 * EPL, ESZ = BF ? 2 : 4;
+  extern __shared__ float4 xs4[];  // [SK * SPW * SPAN], zero past K
+  __shared__ float s_part[kStreamWaves][2];
+  __shared__ float s_red[kStreamWaves];
+  __shared__ float s_rstd;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+  const int KPAD = SK * SPW * SPAN;
+  const int RG = kStreamWaves / SK;
+  const int npairs = (N + 1) / 2;
+  const int pair = blockIdx.x * RG + wave / SK, sw = wave % SK;
+  const int pr = min(pair, npairs - 1);
+  const int r0 = min(pr * 2, N - 1), r1 = min(pr * 2 + 1, N - 1);
+  const char* Wb = (const char*)a.W;
+
+  u32x4 w0[SPW], w1[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int k = min((sw + i * SK) * SPAN + lane * EPL, K - EPL);
+    w0[i] = __builtin_nontemporal_load((const u32x4*)(Wb + ((long long)r0 * K + k) * ESZ));
+    w1[i] = __builtin_nontemporal_load((const u32x4*)(Wb + ((long long)r1 * K + k) * ESZ));
+  }
+  // epilogue operands of the pair
+  float p0 = 0.f, p1 = 0.f;
+  int pos = 0, page = 0;
+  if constexpr (EPI == EPI_RESID) {
+    p0 = a.y[r0];
+    p1 = a.y[r1];
+  }
+  if constexpr (EPI == EPI_EMB) {
+    const int t = min(max(a.tok[a.tok_col], 0), a.tok_rows - 1);
+    p0 = load_w1(a.emb, (long long)t * N + r0, BF);
+    p1 = load_w1(a.emb, (long long)t * N + r1, BF);
+  }
+  if constexpr (EPI == EPI_QKV) {
+    pos = a.pos ? a.pos[0] : a.pos_const;
+    page = a.kv.page_table ? a.kv.page_table[pos / a.kv.pf] : 0;
+    const int dim = (r0 % a.d) % a.hd;
+    const float* cs = a.rope + ((long long)pos * (a.hd >> 1) + (dim >> 1)) * 2;
+    p0 = cs[0];
+    p1 = cs[1];
+  }
+
+  // RMSNorm statistics and the normalised, zero-padded input in LDS
+  float rstd = 1.f;
+  if (a.gain) {
+    float rs = 0.f;
+    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
+      const float4 v = *(const float4*)(a.x + k);
+      rs += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    rs = wave_sum(rs);
+    if (lane == 0) s_red[wave] = rs;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < kStreamWaves; ++w) t += s_red[w];
+      s_rstd = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+    rstd = s_rstd;
+  }
+  for (int k = tid * 4; k < KPAD; k += 64 * kStreamWaves * 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < K) {
+      v = *(const float4*)(a.x + k);
+      if (a.gain) {
+        const float4 g = *(const float4*)(a.gain + k);
+        v.x *= rstd * g.x; v.y *= rstd * g.y; v.z *= rstd * g.z; v.w *= rstd * g.w;
+      }
+    }
+    xs4[k >> 2] = v;
+  }
+  __syncthreads();
+
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int k = (sw + i * SK) * SPAN + lane * EPL;
+    float f0[EPL], f1[EPL], xv[EPL];
+    unpack16<BF>(w0[i], f0);
+    unpack16<BF>(w1[i], f1);
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 t = xs4[(k + e) >> 2];
+      xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      acc0 = fmaf(f0[e], xv[e], acc0);
+      acc1 = fmaf(f1[e], xv[e], acc1);
+    }
+  }
+  acc0 = wave_sum(acc0);
+  acc1 = wave_sum(acc1);
+  if (lane == 0) {
+    s_part[wave][0] = acc0;
+    s_part[wave][1] = acc1;
+  }
+  __syncthreads();
+  if (sw != 0 || lane != 0 || pair >= npairs) return;
+  float t0 = 0.f, t1 = 0.f;
+  for (int w = 0; w < SK; ++w) {
+    t0 += s_part[wave + w][0];
+    t1 += s_part[wave + w][1];
+  }
+  pair_store<EPI>(a, a.y, pair * 2, t0, t1, p0, p1, pos, page);
 }
 
 // ---------------------------------------------------------------------------
@@ -852,8 +981,58 @@ static int device_cus() {
   return cus;
 }
 
+// one input vector and fewer row pairs than kSplitWaves: split K over the
+// waves of a block (k_gemv_splitk); false when the shape does not qualify
+constexpr int kSplitWaves = 2048;
+
+template <bool BF, int SPW>
+static void splitk_launch(const GemvArgs& a, int epi, int SK, hipStream_t s) {
+  constexpr int SPAN = 64 * WLoad<BF>::EPL;
+  const int RG = kStreamWaves / SK;
+  const int npairs = (a.N + 1) / 2;
+  dim3 grid((npairs + RG - 1) / RG);
+  const size_t lds = (size_t)SK * SPW * SPAN * sizeof(float);
+  const int T = 64 * kStreamWaves;
+  switch (epi) {
+    case EPI_STORE: k_gemv_splitk<BF, EPI_STORE, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_RESID: k_gemv_splitk<BF, EPI_RESID, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_EMB: k_gemv_splitk<BF, EPI_EMB, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_SWIGLU: k_gemv_splitk<BF, EPI_SWIGLU, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_QKV: k_gemv_splitk<BF, EPI_QKV, SPW><<<grid, T, lds, s>>>(a, SK); break;
+  }
+}
+
+static bool gemv_splitk(const GemvArgs& a, int epi, bool bf16, hipStream_t s) {
+  const int target = kSplitWaves;
+  const int span = bf16 ? 512 : 256;
+  const int npairs = (a.N + 1) / 2;
+  const int nspans = (a.K + span - 1) / span;
+  if (npairs >= target || a.K % 4 != 0) return false;
+  int SK = 1;
+  while (SK < kStreamWaves && npairs * SK < target && SK * 2 <= nspans) SK *= 2;
+  if (SK < 2) return false;
+  const int need = (nspans + SK - 1) / SK;
+  const int spw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  if (need > 8 || (size_t)SK * spw * span * sizeof(float) > 65536) return false;
+  if (bf16) {
+    if (spw == 1) splitk_launch<true, 1>(a, epi, SK, s);
+    else if (spw == 2) splitk_launch<true, 2>(a, epi, SK, s);
+    else if (spw == 4) splitk_launch<true, 4>(a, epi, SK, s);
+    else splitk_launch<true, 8>(a, epi, SK, s);
+  } else {
+    if (spw == 1) splitk_launch<false, 1>(a, epi, SK, s);
+    else if (spw == 2) splitk_launch<false, 2>(a, epi, SK, s);
+    else if (spw == 4) splitk_launch<false, 4>(a, epi, SK, s);
+    else splitk_launch<false, 8>(a, epi, SK, s);
+  }
+  return true;
+}
+
 template <int NB, bool BF>
 static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s) {
+  if constexpr (NB == 1) {
+    if (gemv_splitk(a, epi, BF, s)) return;
+  }
   if ((size_t)NB * a.K * sizeof(float) <= 65536) {
     const int need = ((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
     dim3 grid(std::min(need, 2 * device_cus()));
