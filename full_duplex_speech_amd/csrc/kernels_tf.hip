@@ -286,152 +286,184 @@ void launch_tf_embed(const EmbedArgs& a, const int* tokens, long long M, int S, 
 }
 
 // ---------------------------------------------------------------------------
-// Causal flash attention over the paged cache (hd = 128, bf16). Block = 4 waves
-// = 128 queries of one (b, head); wave w owns queries q0 + 32w .. +31. Key
-// tiles of 64 are staged in LDS (K as rows, V transposed); per tile each wave
-// computes S = Q K^T with 16 MFMAs (Q fragments stay in registers), applies
-// the causal mask and an online softmax per query row (row statistics reduced
-// across the 32 lanes that hold a row's keys), writes P as bf16 to LDS and
-// accumulates O += P V with 16 more MFMAs. Key tiles above the diagonal are
-// skipped.
+// Causal flash attention over the paged cache (bf16 K/V, fp16 Q and output).
+// Block = 4 waves = 128 queries of one (b, head); wave w owns queries
+// q0 + 32w .. +31. Key tiles of 64 are staged in LDS (K as rows, V
+// transposed); the next tile's K and V wait in registers while the current
+// tile is computed. The matrix cores compute the transposed scores
+// S^T = K Q^T, so each lane holds 32 scores of one query (the other 32 keys of
+// the tile sit in lane l ^ 32) and the online-softmax statistics are in-lane
+// reductions plus one exchange. The probabilities stay in registers as the B
+// operand of O^T += V^T P^T: the contraction runs over the keys in the order
+// the lanes hold them, and V^T is read from LDS in that order. Key tiles above
+// a wave's diagonal are skipped; the longest query tiles are launched first.
 // ---------------------------------------------------------------------------
 constexpr int kFaKT = 64, kFaQT = 128;
-constexpr int kFaVRow = kFaKT + 8;   // V^T tile row
-constexpr int kFaPRow = kFaKT + 8;   // P tile row
+constexpr int kFaVRow = kFaKT + 4;  // V^T tile row (fp16): 34 words, conflict-free 8-byte reads
 
-template <int kFaHD>
-__global__ __launch_bounds__(256) void k_flash_attn(FlashArgs f) {
-  constexpr int kFaKRow = kFaHD + 8;  // K tile row (bf16), padded
-  constexpr int CPR = kFaHD / 8;      // 16-byte chunks per K/V row
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFaKT * kFaKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kFaHD * kFaVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[kFaQT * kFaPRow];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+typedef uint32_t u32x2t __attribute__((ext_vector_type(2)));
+
+template <int HD>
+__global__ __launch_bounds__(256, 2) void k_flash_attn(FlashArgs f) {
+  constexpr int KROW = HD + 8;                    // K tile row (fp16), padded
+  constexpr int CPR = HD / 8;                     // 16-byte chunks per K/V row
+  constexpr int KCH = kFaKT * CPR / 256;          // K chunks per thread and tile
+  constexpr int VCH = (kFaKT / 2) * CPR / 256;    // V (key pair, chunk) units per thread and tile
+  constexpr int TD = HD / 32;                     // 32-dim output blocks
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kFaKT * KROW];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[HD * kFaVRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hl = lane >> 5, ln = lane & 31;
+  const int qt = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int S = f.S;
-  const int q0 = qt * kFaQT;
-  const int qw = q0 + wave * 32;
+  const int q0 = qt * kFaQT, qw = q0 + wave * 32;
+  const int myq = qw + ln;
   const KvView& kv = f.kv;
   const long long head_off = (long long)((f.layer * 2) * kv.n_heads + h) * kv.pf * kv.hd;
   const long long v_off = (long long)kv.n_heads * kv.pf * kv.hd;
+  const uint16_t* kvb = (const uint16_t*)kv.base;
+  // page ids of the keys 0..kend-1, so that tile fetches wait on nothing but themselves
+  __shared__ int pages[kMaxPagesPerConv];
+  const int kend = min(q0 + kFaQT, S);  // keys needed by this query tile
+  for (int i = tid; i <= (kend - 1) / kv.pf; i += 256) pages[i] = kv.page_table[b * kv.pt_stride + i];
+  __syncthreads();
+  auto row_ptr = [&](int key) {
+    return kvb + (long long)pages[key / kv.pf] * kv.page_stride + head_off + (long long)(key % kv.pf) * kv.hd;
+  };
 
-  // Q fragments: lane holds Q[qw + lane%32][16*ks + 8*(lane/32) .. +7]
-  f16x8 qf[kFaHD / 16];
+  // B operand of S^T = K Q^T: lane holds Q[myq][16 ks + 8 hl .. +7]
+  f16x8 qf[HD / 16];
   {
-    const int qrow = min(qw + (lane & 31), S - 1);
-    const uint16_t* qp = f.q + ((long long)b * S + qrow) * f.ldq + h * kFaHD + 8 * (lane >> 5);
+    const uint16_t* qp = f.q + ((long long)b * S + min(myq, S - 1)) * f.ldq + h * HD + 8 * hl;
 #pragma unroll
-    for (int ks = 0; ks < kFaHD / 16; ++ks) qf[ks] = *(const f16x8*)(qp + 16 * ks);
+    for (int ks = 0; ks < HD / 16; ++ks) qf[ks] = *(const f16x8*)(qp + 16 * ks);
   }
-  f32x16 o[kFaHD / 32];
+
+  u32x4t kreg[KCH], vreg[VCH][2];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int t = 0; t < kFaHD / 32; ++t)
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      kreg[i] = *(const u32x4t*)(row_ptr(min(k0 + c / CPR, kend - 1)) + (c % CPR) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i, pr = c & 31, ch = c >> 5;
+      vreg[i][0] = *(const u32x4t*)(row_ptr(min(k0 + 2 * pr, kend - 1)) + v_off + ch * 8);
+      vreg[i][1] = *(const u32x4t*)(row_ptr(min(k0 + 2 * pr + 1, kend - 1)) + v_off + ch * 8);
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4t*)(&Ks[(c / CPR) * KROW + (c % CPR) * 8]) = bf8_to_h8(kreg[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int c = tid + 256 * i, pr = c & 31, ch = c >> 5;
+      const u32x4t v0 = bf8_to_h8(vreg[i][0]), v1 = bf8_to_h8(vreg[i][1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (v0[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        const uint32_t hi = (v1[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        *(uint32_t*)(&Vt[(ch * 8 + e) * kFaVRow + 2 * pr]) = lo | (hi << 16);
+      }
+    }
+  };
+
+  f32x16 o[TD];
+#pragma unroll
+  for (int t = 0; t < TD; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
-  float mrow[16], lrow[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    mrow[r] = -INFINITY;
-    lrow[r] = 0.f;
-  }
-  const float scale = f.scale;
-  const int kend = min(q0 + kFaQT, S);  // keys needed by this query tile
+  float m = -INFINITY, l = 0.f;
+  const float scale2 = f.scale * 1.4426950408889634f;  // log2(e)
+  fetch(0);
   for (int k0 = 0; k0 < kend; k0 += kFaKT) {
-    // stage K and V^T of keys k0 .. k0+63 (clamped to S-1)
+    __syncthreads();  // the previous tile's LDS reads are done
+    stage();
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kFaKT * CPR / 256; ++i) {
-      const int c = tid + 256 * i;
-      const int kr = c / CPR, hc = (c % CPR) * 8;
-      const int key = min(k0 + kr, S - 1);
-      const int page = kv.page_table[b * kv.pt_stride + key / kv.pf];
-      const uint16_t* kp = (const uint16_t*)kv.base + (long long)page * kv.page_stride + head_off +
-                           (long long)(key % kv.pf) * kv.hd + hc;
-      const u32x4t kk = bf8_to_h8(*(const u32x4t*)kp);
-      const u32x4t vv = bf8_to_h8(*(const u32x4t*)(kp + v_off));
-      *(u32x4t*)(&Ks[kr * kFaKRow + hc]) = kk;
-      const uint16_t* ve = (const uint16_t*)&vv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(hc + e) * kFaVRow + kr] = ve[e];
-    }
-    __syncthreads();
+    if (k0 + kFaKT < kend) fetch(k0 + kFaKT);
     if (k0 > qw + 31) continue;  // whole tile above this wave's diagonal
-    // S = Q K^T for keys k0 + 32t + lane%32
+    // S^T: sc[t][r] = S[myq][k0 + 32t + 8(r/4) + 4hl + r%4]
     f32x16 sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[t][r] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < kFaHD / 16; ++ks) {
-        const f16x8 kf = *(const f16x8*)(&Ks[(32 * t + (lane & 31)) * kFaKRow + 16 * ks + 8 * (lane >> 5)]);
-        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qf[ks], kf, sc[t], 0, 0, 0);
+      for (int ks = 0; ks < HD / 16; ++ks) {
+        const f16x8 kf = *(const f16x8*)(&Ks[(32 * t + ln) * KROW + 16 * ks + 8 * hl]);
+        sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sc[t], 0, 0, 0);
       }
     }
-    // C layout: sc[t][r] = S[query qw + 8*(r/4) + 4*(lane/32) + r%4][key k0 + 32t + lane%32]
-    float alpha[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int qrow = qw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key = k0 + 32 * t + (lane & 31);
-        float v = sc[t][r] * scale;
-        v = (key <= qrow && key < S) ? v : -INFINITY;
-        sc[t][r] = v;
-        mx = fmaxf(mx, v);
-      }
-#pragma unroll
-      for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-      const float mn = fmaxf(mrow[r], mx);
-      alpha[r] = mn == -INFINITY ? 1.f : expf(mrow[r] - mn);
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float pv = mn == -INFINITY ? 0.f : expf(sc[t][r] - mn);
-        sc[t][r] = pv;
-        sum += pv;
-      }
-#pragma unroll
-      for (int off = 16; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-      lrow[r] = lrow[r] * alpha[r] + sum;
-      mrow[r] = mn;
-    }
-    // P (bf16) to LDS rows of this wave: P[q - q0][key - k0]
+    // scores in log2 units (scale * log2 e), so that exp(x) = 2^(x log2 e)
+    // is one hardware exp2; only tiles that reach the diagonal or the end of
+    // the sequence need the mask
+    const bool masked = k0 + kFaKT - 1 > qw || k0 + kFaKT > S;
+    float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ql = wave * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        Ps[ql * kFaPRow + 32 * t + (lane & 31)] = tf_f2h(sc[t][r]);
+        float v = sc[t][r] * scale2;
+        if (masked) {
+          const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hl + (r & 3);
+          v = (key <= myq && key < S) ? v : -INFINITY;
+        }
+        sc[t][r] = v;
+        mx = fmaxf(mx, v);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+    float sum = 0.f;
 #pragma unroll
-    for (int t = 0; t < kFaHD / 32; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= alpha[r];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): P stores done before the wave reads them
-    __builtin_amdgcn_wave_barrier();
-    // O += P V: A = P[q][16ks + 8*(lane/32) ..], B = V[16ks + 8*(lane/32) + i][32t + lane%32]
+      for (int r = 0; r < 16; ++r) {
+        const float pv = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[t][r] - mn);
+        sc[t][r] = pv;
+        sum += pv;
+      }
+    sum += __shfl_xor(sum, 32, 64);
+    l = l * alpha + sum;
+    m = mn;
+#pragma unroll
+    for (int t = 0; t < TD; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    // O^T += V^T P^T over 4 steps of 16 keys; step ks holds the keys of
+    // sc[ks / 2][8 (ks % 2) .. +7], i.e. k0 + 32 (ks/2) + 16 (ks%2) + 8 (i/4) + 4 hl + i%4
 #pragma unroll
     for (int ks = 0; ks < kFaKT / 16; ++ks) {
-      const f16x8 pf = *(const f16x8*)(&Ps[(wave * 32 + (lane & 31)) * kFaPRow + 16 * ks + 8 * (lane >> 5)]);
+      const int t = ks >> 1, rb = 8 * (ks & 1);
+      f16x8 pf;
 #pragma unroll
-      for (int t = 0; t < kFaHD / 32; ++t) {
-        const f16x8 vf = *(const f16x8*)(&Vt[(32 * t + (lane & 31)) * kFaVRow + 16 * ks + 8 * (lane >> 5)]);
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(pf, vf, o[t], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) pf[i] = (_Float16)sc[t][rb + i];
+#pragma unroll
+      for (int td = 0; td < TD; ++td) {
+        const uint16_t* vp = &Vt[(32 * td + ln) * kFaVRow + 32 * t + 16 * (ks & 1) + 4 * hl];
+        const u32x2t a0 = *(const u32x2t*)vp, a1 = *(const u32x2t*)(vp + 8);
+        u32x4t av;
+        av[0] = a0[0]; av[1] = a0[1]; av[2] = a1[0]; av[3] = a1[1];
+        o[td] = __builtin_amdgcn_mfma_f32_32x32x16_f16(*(const f16x8*)&av, pf, o[td], 0, 0, 0);
       }
     }
   }
-  // O / l -> bf16 out[b*S + q][h*hd + 32t + lane%32]
+  // O^T: o[td][r] = O[myq][32 td + 8 (r/4) + 4 hl + r%4]
+  if (myq < S) {
+    const float inv = 1.f / l;
+    uint16_t* op = f.out + ((long long)b * S + myq) * f.ldo + h * HD + 4 * hl;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int qrow = qw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (qrow >= S) continue;
-    const float inv = 1.f / lrow[r];
-    uint16_t* op = f.out + ((long long)b * S + qrow) * f.ldo + h * kFaHD + (lane & 31);
+    for (int td = 0; td < TD; ++td)
 #pragma unroll
-    for (int t = 0; t < kFaHD / 32; ++t) op[32 * t] = tf_f2h(o[t][r] * inv);
+      for (int g = 0; g < 4; ++g) {
+        u32x2t w;
+        w[0] = (uint32_t)tf_f2h(o[td][4 * g] * inv) | ((uint32_t)tf_f2h(o[td][4 * g + 1] * inv) << 16);
+        w[1] = (uint32_t)tf_f2h(o[td][4 * g + 2] * inv) | ((uint32_t)tf_f2h(o[td][4 * g + 3] * inv) << 16);
+        *(u32x2t*)(op + 32 * td + 8 * g) = w;
+      }
   }
 }
 
