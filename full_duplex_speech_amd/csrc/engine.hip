@@ -93,6 +93,7 @@ struct Plan {
   size_t tf_tokens = 0, tf_ce = 0, tf_res = 0;
   long long tf_max = 0;
   bool tf_mfma = false;  // matrix-core teacher-forced pass (bf16 models)
+  size_t w16 = 0;  // fp16 mirror of the weight region [0, meta_row0) for the matrix-core pass
   size_t tf_H = 0, tf_Xn = 0, tf_I = 0, tf_Q = 0, tf_O = 0, tf_text = 0;
   size_t tf_U = 0, tf_Xd = 0, tf_DQ = 0, tf_DK = 0, tf_DV = 0, tf_DO = 0, tf_DI = 0, tf_audio = 0;
   size_t staging = 0, staging_bytes = 0;
@@ -223,6 +224,7 @@ Plan make_plan(const moshi_config& c) {
               hdd <= 64;
   if (p.tf_mfma) {
     const size_t T = (size_t)tf;
+    p.w16 = p.take(p.meta_row0);
     p.tf_H = p.take(T * d * 4);
     p.tf_Xn = p.take(T * d * 2);
     p.tf_I = p.take(T * F * 2);
@@ -612,7 +614,7 @@ void enqueue_tf_mfma(moshi_ctx* c, const int* tok, int B, int S, bool depth, flo
   const KvView tkv = temporal_kv(c);
   auto gemm = [&](const void* W, const uint16_t* X, long long ldx, int N, int K) {
     GemmArgs a{};
-    a.W = (const uint16_t*)W;
+    a.W = c->at<uint16_t>(p.w16 + (size_t)((const char*)W - c->ws));  // fp16 copy of the weight
     a.X = X;
     a.ldx = ldx;
     a.M = (int)M;
@@ -954,6 +956,12 @@ int moshi_init_weights(moshi_ctx* c, const moshi_tensor* t, int n) {
           HIPCHECK(hipGetLastError());
           HIPCHECK(hipStreamSynchronize(c->stream));
         }
+      }
+      if (bf && p.tf_mfma) {
+        // the matrix-core pass reads an fp16 copy (same rounding as converting in the GEMM)
+        launch_bf16_to_f16((const uint16_t*)dst, c->at<uint16_t>(p.w16 + ds.off), ds.rows * ds.mult * ds.cols,
+                           c->stream);
+        HIPCHECK(hipGetLastError());
       }
       if (!ds.loaded) {
         ds.loaded = true;

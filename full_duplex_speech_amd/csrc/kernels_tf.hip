@@ -17,6 +17,8 @@
 
 #include <math.h>
 
+#include <stdexcept>
+
 #include "moshi_internal.h"
 
 namespace moshi {
@@ -48,7 +50,7 @@ __device__ __forceinline__ u32x4t bf8_to_h8(u32x4t v) {
 }
 
 // ---------------------------------------------------------------------------
-// C[m][n] = sum_k X[m][k] W[n][k]  (X fp16 [M][ldx], W bf16 [N][K], K % 32 == 0)
+// C[m][n] = sum_k X[m][k] W[n][k]  (X fp16 [M][ldx], W fp16 [N][K], K % 64 == 0)
 //
 // The matrix core computes the transposed tile W_tile * X_tile^T: A operand =
 // 32 rows of W, B operand = 32 rows of X, both read as 16-byte runs along K.
@@ -57,15 +59,24 @@ __device__ __forceinline__ u32x4t bf8_to_h8(u32x4t v) {
 // one lane and rows are written as 8- or 16-byte runs.
 //
 // Block: 256 threads = 4 waves in a 2 (n) x 2 (m) arrangement, each wave a
-// 64 x 64 tile (2 x 2 MFMA tiles), block tile 128 (n) x 128 (m), K step 32,
-// LDS double buffer filled from registers that are loaded one step ahead.
-// Blocks are ordered in groups of 8 tiles along m so that concurrently running
-// blocks share both operand panels in L2.
+// (32 WT) x 64 tile (WT x 2 MFMA tiles), block tile (64 WT) (n) x 128 (m), K
+// step kTK (64 where K allows), LDS double buffer filled from two register
+// sets, so each step's loads are issued two steps before they are stored.
+// WT = 2 measured best: the wider wave tile (WT = 4) needs 272+ registers and
+// runs one wave per SIMD. Weights come from an fp16 copy made at upload, so
+// both operands go to LDS without conversion. Blocks are ordered in groups of
+// 8 tiles along m so that concurrently running blocks share both operand
+// panels in L2.
 // ---------------------------------------------------------------------------
-constexpr int kTN = 128, kTM = 128, kTK = 32, kLdsRow = kTK + 8;  // padded row: 80 bytes
+constexpr int kTM = 128;
 
-template <int EPI>
+template <int EPI, int WT, int kTK>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+  constexpr int kTN = 64 * WT;
+  constexpr int kLdsRow = kTK + 8;        // padded row (fp16)
+  constexpr int CPRW = kTK / 8;           // 16-byte chunks per row and K step
+  constexpr int WCH = kTN * CPRW / 256;   // W chunks per thread and K step
+  constexpr int XCH = kTM * CPRW / 256;   // X chunks per thread and K step
   __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kTN * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint16_t Xs[2][kTM * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -81,50 +92,60 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
   const int tn = (blockIdx.x % per_group) / gsize;
   const int n0 = tn * kTN, m0 = tm * kTM;
 
-  // global -> register loads: 2 chunks of 8 bf16 per thread for each operand
-  u32x4t rw[2], rx[2];
-  auto gload = [&](int k0) {
+  // global -> register loads: WCH chunks of 8 fp16 of W and 2 of X per thread
+  // and K step, in two register sets: the loads of step kt + 2 are issued
+  // while step kt is computed, so each has two steps of work to land. Steps
+  // past the end re-read the last step (valid addresses, results unused), so
+  // the loop carries no conditional loads.
+  struct Regs {
+    u32x4t w[WCH], x[XCH];
+  };
+  Regs ra, rb;
+  const int nk = K / kTK;
+  auto gload = [&](Regs& r, int kt) {
+    const int k0 = min(kt, nk - 1) * kTK;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WCH; ++i) {
       const int c = tid + 256 * i;
-      const int row = c >> 2, kc = (c & 3) * 8;
-      const int n = min(n0 + row, N - 1), m = min(m0 + row, M - 1);
-      rw[i] = *(const u32x4t*)(g.W + (long long)n * K + k0 + kc);
-      rx[i] = *(const u32x4t*)(g.X + (long long)m * g.ldx + k0 + kc);
+      const int row = c / CPRW, kc = (c % CPRW) * 8;
+      r.w[i] = *(const u32x4t*)(g.W + (long long)min(n0 + row, N - 1) * K + k0 + kc);
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + 256 * i;
+      const int row = c / CPRW, kc = (c % CPRW) * 8;
+      r.x[i] = *(const u32x4t*)(g.X + (long long)min(m0 + row, M - 1) * g.ldx + k0 + kc);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const Regs& r, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < WCH; ++i) {
       const int c = tid + 256 * i;
-      const int row = c >> 2, kc = (c & 3) * 8;
-      *(u32x4t*)(&Ws[buf][row * kLdsRow + kc]) = bf8_to_h8(rw[i]);
-      *(u32x4t*)(&Xs[buf][row * kLdsRow + kc]) = rx[i];
+      *(u32x4t*)(&Ws[buf][(c / CPRW) * kLdsRow + (c % CPRW) * 8]) = r.w[i];
+    }
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + 256 * i;
+      *(u32x4t*)(&Xs[buf][(c / CPRW) * kLdsRow + (c % CPRW) * 8]) = r.x[i];
     }
   };
 
   const int wn = wave >> 1, wm = wave & 1;
-  f32x16 acc[2][2];
+  f32x16 acc[WT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / kTK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kTK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < kTK / 16; ++ks) {
-      f16x8 a[2], b[2];
+      f16x8 a[WT], b[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wn * 64 + i * 32 + (lane & 31);
+      for (int i = 0; i < WT; ++i) {
+        const int row = wn * (32 * WT) + i * 32 + (lane & 31);
         a[i] = *(const f16x8*)(&Ws[buf][row * kLdsRow + ks * 16 + (lane >> 5) * 8]);
       }
 #pragma unroll
@@ -133,27 +154,44 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
         b[j] = *(const f16x8*)(&Xs[buf][row * kLdsRow + ks * 16 + (lane >> 5) * 8]);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
+  };
+
+  // nk is even (K % (2 kTK) == 0): the loop body is two steps and has no exits;
+  // the last stores write re-read data that nothing reads
+  gload(ra, 0);
+  gload(rb, 1);
+  lstore(ra, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    // step kt from LDS buffer 0; rb holds step kt + 1
+    gload(ra, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the wait for rb
+    compute(0);
+    lstore(rb, 1);
+    __syncthreads();
+    // step kt + 1 from buffer 1; ra holds step kt + 2
+    gload(rb, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1);
+    lstore(ra, 0);
+    __syncthreads();
   }
 
   // epilogue: lane holds token m = m0 + wm*64 + j*32 + lane%32 and features
-  // n = n0 + wn*64 + i*32 + 8*q + 4*(lane/32) + t, for q, t in 0..3
+  // n = n0 + wn*32*WT + i*32 + 8*q + 4*(lane/32) + t, for q, t in 0..3
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < WT; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int m = m0 + wm * 64 + j * 32 + (lane & 31);
       if (m >= M) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+        const int n = n0 + wn * (32 * WT) + i * 32 + 8 * q + 4 * (lane >> 5);
         if (n >= N) continue;
         float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         if constexpr (EPI == TF_STORE_F32) {
@@ -211,15 +249,38 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
   }
 }
 
-void launch_gemm_bf16(const GemmArgs& g, int epi, hipStream_t s) {
-  const int tiles = ((g.N + kTN - 1) / kTN) * ((g.M + kTM - 1) / kTM);
+// fp16 copy of bf16 weights for the matrix-core pass
+__global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* src, uint16_t* dst, long long n) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256)
+    dst[i] = tf_f2h(tf_bf2f(src[i]));
+}
+
+void launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, long long n, hipStream_t s) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  k_bf16_to_f16<<<(unsigned)blocks, 256, 0, s>>>(src, dst, n);
+}
+
+template <int WT, int KT>
+static void gemm_launch(const GemmArgs& g, int epi, hipStream_t s) {
+  const int tiles = ((g.N + 64 * WT - 1) / (64 * WT)) * ((g.M + kTM - 1) / kTM);
   switch (epi) {
-    case TF_STORE_F32: k_gemm_bf16<TF_STORE_F32><<<tiles, 256, 0, s>>>(g); break;
-    case TF_RESID: k_gemm_bf16<TF_RESID><<<tiles, 256, 0, s>>>(g); break;
-    case TF_EMB: k_gemm_bf16<TF_EMB><<<tiles, 256, 0, s>>>(g); break;
-    case TF_SWIGLU: k_gemm_bf16<TF_SWIGLU><<<tiles, 256, 0, s>>>(g); break;
-    case TF_QKV: k_gemm_bf16<TF_QKV><<<tiles, 256, 0, s>>>(g); break;
+    case TF_STORE_F32: k_gemm_bf16<TF_STORE_F32, WT, KT><<<tiles, 256, 0, s>>>(g); break;
+    case TF_RESID: k_gemm_bf16<TF_RESID, WT, KT><<<tiles, 256, 0, s>>>(g); break;
+    case TF_EMB: k_gemm_bf16<TF_EMB, WT, KT><<<tiles, 256, 0, s>>>(g); break;
+    case TF_SWIGLU: k_gemm_bf16<TF_SWIGLU, WT, KT><<<tiles, 256, 0, s>>>(g); break;
+    case TF_QKV: k_gemm_bf16<TF_QKV, WT, KT><<<tiles, 256, 0, s>>>(g); break;
   }
+}
+
+void launch_gemm_bf16(const GemmArgs& g, int epi, hipStream_t s) {
+  if (g.K % 64 != 0 || g.K <= 0) throw std::runtime_error("teacher-forced GEMM needs K % 64 == 0");
+  // 64-wide K steps need an even number of them
+  if (g.K % 128 == 0)
+    gemm_launch<2, 64>(g, epi, s);
+  else
+    gemm_launch<2, 32>(g, epi, s);
 }
 
 // ---------------------------------------------------------------------------

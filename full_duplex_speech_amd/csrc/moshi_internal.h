@@ -120,8 +120,8 @@ struct CeRowsArgs {
 enum TfEpi { TF_STORE_F32 = 0, TF_RESID = 1, TF_EMB = 2, TF_SWIGLU = 3, TF_QKV = 4 };
 
 struct GemmArgs {
-  const uint16_t* W;  // [N][K] bf16
-  const uint16_t* X;  // [M][ldx] bf16
+  const uint16_t* W;  // [N][K] fp16 (copy of the bf16 weight)
+  const uint16_t* X;  // [M][ldx] fp16
   long long ldx;
   int M, N, K;
   float* Yf;          // float32 output / residual stream [M][ldy]
@@ -180,6 +180,8 @@ void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, h
 void launch_embed(const EmbedArgs& a, int B, bool bf16, hipStream_t s);
 void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s);
 void launch_advance(const AdvanceArgs& a, int B, hipStream_t s);
+// bf16 -> fp16 element copy (round to nearest even; |x| > 65504 -> inf)
+void launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, long long n, hipStream_t s);
 void launch_convert(const float* src, long long rows, int cols, void* dst, bool bf16, long long dst_row_mult,
                     long long dst_row_add, hipStream_t s);
 // launchers (kernels_loss.hip)
