@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 matrix-core peak of one MI355X
 COUNTERS = os.path.join(ROOT, "profiles", "gemv_gate_up_b1_7b_counters.md")
 KERNEL_SRC = os.path.join(ROOT, "full_duplex_speech_amd", "csrc", "kernels_decode.hip")
 
@@ -37,6 +38,20 @@ def measured_traffic():
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def tf_pass_flops(cfg, B, S):
+    """Algorithmic floating-point operations of one teacher-forced pass over B x S frames: every
+    linear map of the temporal and depth models, the text and depth heads, and causal attention
+    over the S(S+1)/2 key-query pairs (QK^T and PV); the depth attention over <= 8 positions is
+    negligible and not counted."""
+    M = B * S
+    d, F, dd, Fd = cfg.d_t, cfg.ffn_t, cfg.d_d, cfg.ffn_d
+    temporal = 2.0 * M * cfg.n_layers_t * (4 * d * d + 3 * d * F)
+    head = 2.0 * M * cfg.vocab_text * d
+    attn = 4.0 * B * cfg.n_layers_t * d * S * (S + 1) / 2
+    depth = 2.0 * M * cfg.n_q * (dd * d + cfg.n_layers_d * (4 * dd * dd + 3 * dd * Fd) + cfg.codebook * dd)
+    return temporal + head + attn + depth
 
 
 def log(msg):
@@ -175,9 +190,24 @@ def main():
     ms_per_step = dt * 1000 / K
     value = frames_per_step * K / dt
 
-    # dominant kernel: the SwiGLU gate/up weight stream (the largest share of the frame's bytes)
+    # dominant kernel: the SwiGLU gate/up weight stream (the largest share of the frame's bytes);
+    # in the teacher-forced pass the gate/up GEMM (the largest share of the pass's FLOPs)
     roofline = None
-    if not tf_mode:
+    if tf_mode:
+        us, flops = fds.moshi_time_kernel(ctx, "tf_gate_up", B, 8)
+        ach = flops / (us * 1e-6) / 1e12
+        aus, aflops = fds.moshi_time_kernel(ctx, "tf_attn", B, 8)
+        pass_flops = tf_pass_flops(cfg, B, cfg.tf_frames)
+        pass_tflops = pass_flops / (ms_per_step * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "k_gemm_bf16 (gate/up GEMM + SiLU product, one temporal layer)",
+                    "flops_per_launch": flops, "us_per_launch": round(us, 1),
+                    "other_kernels": {"tf_attn": {"us": round(aus, 1),
+                                                  "TFLOP/s": round(aflops / (aus * 1e-6) / 1e12, 1)}},
+                    "pass_flops": pass_flops, "pass_tflops": round(pass_tflops, 1),
+                    "pass_frac": round(pass_tflops / MFMA_PEAK_TFLOPS, 4)}
+    else:
         us, nbytes = fds.moshi_time_kernel(ctx, "ffn_gate_up", B, args.kernel_iters)
         ach = nbytes / (us * 1e-6) / 1e9
         traffic = measured_traffic() if (cfg.name == "b1_7b" and B == 1) else None

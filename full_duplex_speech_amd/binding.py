@@ -58,7 +58,8 @@ EXPORTS = (
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
     "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel",
 )
-KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5}
+KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5, "tf_gate_up": 6,
+           "tf_attn": 7}
 
 _lib = None
 
@@ -211,7 +212,8 @@ def moshi_undelay_codes(model: np.ndarray, tau: int) -> np.ndarray:
 
 
 def moshi_time_kernel(ctx, kernel: str, batch: int, iters: int) -> Tuple[float, float]:
-    """(mean microseconds per launch, algorithmic bytes per launch) of one frame kernel."""
+    """(mean microseconds per launch, algorithmic work per launch) of one kernel: bytes for the frame
+    kernels, floating-point operations for the teacher-forced ones ("tf_gate_up", "tf_attn")."""
     us = ctypes.c_float()
     nbytes = ctypes.c_double()
     _check(ctx, lib().moshi_time_kernel(ctx, KERNELS[kernel], batch, iters, ctypes.byref(us), ctypes.byref(nbytes)))

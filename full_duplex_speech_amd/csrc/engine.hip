@@ -261,6 +261,7 @@ struct moshi_ctx {
   bool ready = false;
   bool use_graph = true;
   bool tf_steps = false;  // teacher-forced pass as forced frame steps even for bf16 models
+  int tf_B = 0, tf_S = 0;  // shape of the last matrix-core teacher-forced pass
   std::map<std::pair<int, int>, hipGraphExec_t> graphs;
   // host mirrors
   std::vector<int> pos_h;
@@ -582,6 +583,33 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   HIPCHECK(hipGetLastError());
 }
 
+// operands of one teacher-forced GEMM over M frames: the fp16 copy of weight W
+GemmArgs tf_gemm_args(moshi_ctx* c, const void* W, const uint16_t* X, long long ldx, long long M, int N, int K) {
+  GemmArgs a{};
+  a.W = c->at<uint16_t>(c->plan.w16 + (size_t)((const char*)W - c->ws));
+  a.X = X;
+  a.ldx = ldx;
+  a.M = (int)M;
+  a.N = N;
+  a.K = K;
+  return a;
+}
+
+// causal flash attention of temporal layer l over S frames of each conversation
+FlashArgs tf_flash_args(moshi_ctx* c, int l, int S) {
+  const int d = c->cfg.d_t;
+  FlashArgs fa{};
+  fa.q = c->at<uint16_t>(c->plan.tf_Q);
+  fa.ldq = d;
+  fa.kv = temporal_kv(c);
+  fa.layer = l;
+  fa.S = S;
+  fa.scale = 1.0f / sqrtf((float)(d / c->cfg.n_heads_t));
+  fa.out = c->at<uint16_t>(c->plan.tf_O);
+  fa.ldo = d;
+  return fa;
+}
+
 // Teacher-forced pass on matrix cores (bf16 models): every linear map is one
 // GEMM over the B*S frames; attention is causal flash attention over the KV
 // pages of conversations 0..B-1; the Depth Transformer runs layer by layer over
@@ -613,14 +641,7 @@ void enqueue_tf_mfma(moshi_ctx* c, const int* tok, int B, int S, bool depth, flo
 
   const KvView tkv = temporal_kv(c);
   auto gemm = [&](const void* W, const uint16_t* X, long long ldx, int N, int K) {
-    GemmArgs a{};
-    a.W = c->at<uint16_t>(p.w16 + (size_t)((const char*)W - c->ws));  // fp16 copy of the weight
-    a.X = X;
-    a.ldx = ldx;
-    a.M = (int)M;
-    a.N = N;
-    a.K = K;
-    return a;
+    return tf_gemm_args(c, W, X, ldx, M, N, K);
   };
   for (int l = 0; l < g.n_layers_t; ++l) {
     const LayerW& w = p.lt[l];
@@ -637,16 +658,7 @@ void enqueue_tf_mfma(moshi_ctx* c, const int* tok, int B, int S, bool depth, flo
     q.kv_paged = 1;
     q.layer = l;
     launch_gemm_bf16(q, TF_QKV, s);
-    FlashArgs fa{};
-    fa.q = Q;
-    fa.ldq = d;
-    fa.kv = tkv;
-    fa.layer = l;
-    fa.S = S;
-    fa.scale = 1.0f / sqrtf((float)hdt);
-    fa.out = O;
-    fa.ldo = d;
-    launch_flash_attn(fa, B, g.n_heads_t, hdt, s);
+    launch_flash_attn(tf_flash_args(c, l, S), B, g.n_heads_t, hdt, s);
     GemmArgs o = gemm(c->ws + w.wo, O, d, d, d);
     o.Yf = H;
     o.ldy = d;
@@ -1064,6 +1076,8 @@ int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B,
     const hipMemcpyKind k = dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
     if (p.tf_mfma && !c->tf_steps) {
       enqueue_tf_mfma(c, tok, B, S, depth, dev ? text_logits : nullptr, dev ? audio_logits : nullptr, loss != nullptr);
+      c->tf_B = B;
+      c->tf_S = S;
       if (!dev) {
         if (text_logits)
           HIPCHECK(hipMemcpyAsync(text_logits, c->ws + p.tf_text, (size_t)B * S * g.vocab_text * 4, k, s));
@@ -1144,9 +1158,14 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
     if (!c->ready) fail(MOSHI_ESTATE, "weights not loaded");
     if (batch < 1 || batch > g.max_batch) fail(MOSHI_EINVAL, "batch %d out of range", batch);
     if (iters < 1 || !avg_us || !bytes_per_launch) fail(MOSHI_EINVAL, "bad iters or output pointers");
-    if (kernel < 0 || kernel > MOSHI_KERNEL_ATTN) fail(MOSHI_EINVAL, "unknown kernel id %d", kernel);
+    if (kernel < 0 || kernel > MOSHI_KERNEL_TF_ATTN) fail(MOSHI_EINVAL, "unknown kernel id %d", kernel);
+    const bool tf = kernel >= MOSHI_KERNEL_TF_GATE_UP;
+    if (tf && (!p.tf_mfma || c->tf_B == 0)) fail(MOSHI_ESTATE, "no matrix-core teacher-forced pass to time");
+    if (tf && batch != c->tf_B) fail(MOSHI_EINVAL, "batch %d differs from the last teacher-forced pass (%d)", batch, c->tf_B);
     const double e = p.esz;
     const double d = g.d_t, F = g.ffn_t, B = batch;
+    const long long tfM = (long long)c->tf_B * c->tf_S;
+    const double S = c->tf_S;
     for (int b = 0; b < batch; ++b)
       if (kernel == MOSHI_KERNEL_ATTN && c->pos_h[b] < 1) fail(MOSHI_ESTATE, "attention timing needs a filled cache");
     double bytes = 0;
@@ -1185,6 +1204,18 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
           bytes = keys * 2 * d * (p.bf ? 2 : 4) + B * 2 * d * 4;
           break;
         }
+        case MOSHI_KERNEL_TF_GATE_UP: {
+          GemmArgs gu = tf_gemm_args(c, c->ws + w.wgu, c->at<uint16_t>(p.tf_Xn), g.d_t, tfM, 2 * g.ffn_t, g.d_t);
+          gu.Yb = c->at<uint16_t>(p.tf_I);
+          gu.ldy = g.ffn_t;
+          launch_gemm_bf16(gu, TF_SWIGLU, c->stream);
+          bytes = 2.0 * (double)tfM * 2 * F * d;  // floating-point operations
+          break;
+        }
+        case MOSHI_KERNEL_TF_ATTN:
+          launch_flash_attn(tf_flash_args(c, l, c->tf_S), batch, g.n_heads_t, g.d_t / g.n_heads_t, c->stream);
+          bytes = 4.0 * B * d * S * (S + 1) / 2;  // QK^T and PV over the causal pairs
+          break;
       }
     };
     if (kernel == MOSHI_KERNEL_QKV)

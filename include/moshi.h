@@ -164,14 +164,22 @@ int moshi_forward_teacher_forced(moshi_ctx* ctx, const int32_t* tokens, int32_t 
 #define MOSHI_KERNEL_FFN_DOWN 3   /* down projection + residual, one temporal layer */
 #define MOSHI_KERNEL_TEXT_HEAD 4  /* final RMSNorm + text head */
 #define MOSHI_KERNEL_ATTN 5       /* causal decode attention over the filled cache, one layer */
+#define MOSHI_KERNEL_TF_GATE_UP 6 /* teacher-forced gate/up GEMM + SiLU product, one temporal layer */
+#define MOSHI_KERNEL_TF_ATTN 7    /* teacher-forced causal flash attention, one temporal layer */
 
-/* Measurement: launch one kernel of the frame `iters` times on the context
- * stream, cycling over the temporal layers' weights (so that weights come from
- * HBM as in a real frame), between two HIP events; returns the mean time per
- * launch in microseconds and the algorithmic bytes one launch must move
- * (weights, plus activations, plus K/V for attention). Uses the current
- * activations and, for attention, the filled KV cache (position >= 1). The
- * conversation state is left unchanged except for scratch activations. */
+/* Measurement: launch one kernel `iters` times on the context stream, cycling
+ * over the temporal layers' weights (so that weights come from HBM as in a real
+ * frame), between two HIP events; returns the mean time per launch in
+ * microseconds and the algorithmic work of one launch in *bytes_per_launch:
+ *   ids 0-5 (frame step, weight-streaming): bytes one launch must move
+ *     (weights, plus activations, plus K/V for attention); they use the
+ *     current activations and, for attention, the filled KV cache
+ *     (position >= 1);
+ *   ids 6-7 (teacher-forced pass, matrix cores): floating-point operations of
+ *     one launch at the B x S shape of the last moshi_forward_teacher_forced
+ *     call of this context, whose B `batch` must equal (attention counts the
+ *     S(S+1)/2 causal pairs only).
+ * The conversation state is left unchanged except for scratch activations. */
 int moshi_time_kernel(moshi_ctx* ctx, int32_t kernel, int32_t batch, int32_t iters, float* avg_us,
                       double* bytes_per_launch);
 
