@@ -87,7 +87,9 @@ struct Plan {
          st_cnt_d = 0, st_end = 0;
   size_t st_user = 0, st_force = 0, st_has_force = 0;
   // activations (float32)
-  size_t h = 0, q = 0, attn = 0, inter = 0, part_t = 0, text_logits = 0;
+  size_t h = 0, q = 0, attn = 0, inter = 0, inter16 = 0, dinter16 = 0, part_t = 0, text_logits = 0;
+  size_t hstat = 0, dstat = 0;  // per-16-row sums of squares of h / hd (batched steps)
+  int hstat_ld = 0, dstat_ld = 0;
   size_t hd = 0, dq = 0, dattn = 0, dinter = 0, part_d = 0, audio_logits = 0;
   // teacher-forced
   size_t tf_tokens = 0, tf_ce = 0, tf_res = 0;
@@ -204,12 +206,18 @@ Plan make_plan(const moshi_config& c) {
   p.q = p.take(mb * d * 4);
   p.attn = p.take(mb * d * 4);
   p.inter = p.take(mb * F * 4);
+  p.inter16 = p.take(mb * F * 2);  // fp16 copy: input of the batched down projection
+  p.hstat_ld = (int)((d + 15) / 16);
+  p.hstat = p.take((size_t)mb * p.hstat_ld * 4);
+  p.dstat_ld = (int)((dd + 15) / 16);
+  p.dstat = p.take((size_t)mb * p.dstat_ld * 4);
   p.part_t = p.take((size_t)mb * c.n_heads_t * p.max_splits * (hdt + 2) * 4);
   p.text_logits = p.take((size_t)mb * c.vocab_text * 4);
   p.hd = p.take(mb * dd * 4);
   p.dq = p.take(mb * dd * 4);
   p.dattn = p.take(mb * dd * 4);
   p.dinter = p.take(mb * Fd * 4);
+  p.dinter16 = p.take(mb * Fd * 2);
   p.part_d = p.take((size_t)mb * c.n_heads_d * (hdd + 2) * 4);
   p.audio_logits = p.take((size_t)mb * c.n_q * c.codebook * 4);
   // teacher-forced
@@ -438,6 +446,7 @@ GemvArgs gu_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
   f.ldx = D;
   f.gain = c->at<float>(w.ffn_norm);
   f.y = c->at<float>(depth_model ? p.dinter : p.inter);
+  f.y16 = c->at<uint16_t>(depth_model ? p.dinter16 : p.inter16);
   f.ldy = F;
   return f;
 }
@@ -451,6 +460,7 @@ GemvArgs down_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
   dn.N = D;
   dn.K = F;
   dn.x = c->at<float>(depth_model ? p.dinter : p.inter);
+  dn.x16 = c->at<uint16_t>(depth_model ? p.dinter16 : p.inter16);  // written by every SwiGLU epilogue
   dn.ldx = F;
   dn.y = c->at<float>(depth_model ? p.hd : p.h);
   dn.ldy = D;
@@ -499,6 +509,26 @@ ArgmaxArgs argmax_args(moshi_ctx* c, int slot) {
 }
 
 // Enqueue one frame for conversations 0..B-1 (no host interaction).
+// Batched bf16 steps (matrix-core GEMVs) pass the RMSNorm statistics of the
+// residual streams from the kernel that writes them to the next normalising
+// one instead of re-reading the vectors. Producers: the embedding (one partial
+// per 256 features), residual GEMVs and the depth input projection (one per 16
+// rows).
+bool stats_on(moshi_ctx* c, int B) { return c->plan.bf && B >= 2; }
+void stat_consume(moshi_ctx* c, GemvArgs& a, int B, bool depth_model, int n) {
+  if (!stats_on(c, B)) return;
+  const Plan& p = c->plan;
+  a.stat_in = c->at<float>(depth_model ? p.dstat : p.hstat);
+  a.stat_in_ld = depth_model ? p.dstat_ld : p.hstat_ld;
+  a.stat_in_n = n;
+}
+void stat_produce(moshi_ctx* c, GemvArgs& a, int B, bool depth_model) {
+  if (!stats_on(c, B)) return;
+  const Plan& p = c->plan;
+  a.stat_out = c->at<float>(depth_model ? p.dstat : p.hstat);
+  a.stat_out_ld = depth_model ? p.dstat_ld : p.hstat_ld;
+}
+
 void enqueue_step(moshi_ctx* c, int B, bool depth) {
   const moshi_config& g = c->cfg;
   const Plan& p = c->plan;
@@ -514,18 +544,33 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   ea.h = c->at<float>(p.h);
   ea.d = g.d_t;
   ea.err = c->at<int>(p.st_err);
+  if (stats_on(c, B)) {
+    ea.stat_out = c->at<float>(p.hstat);
+    ea.stat_ld = p.hstat_ld;
+  }
   launch_embed(ea, B, bf, s);
+  const int nh = p.hstat_ld, nd = p.dstat_ld;  // partials of a residual GEMV producer
 
   for (int l = 0; l < g.n_layers_t; ++l) {
     const LayerW& w = p.lt[l];
-    launch_gemv(qkv_args(c, w, l, false, 0), B, EPI_QKV, bf, s);    // RMSNorm, Wqkv, RoPE, KV append
+    GemvArgs qa = qkv_args(c, w, l, false, 0);  // RMSNorm, Wqkv, RoPE, KV append
+    stat_consume(c, qa, B, false, l == 0 ? (g.d_t + 255) / 256 : nh);
+    launch_gemv(qa, B, EPI_QKV, bf, s);
     launch_attn_decode(attn_args(c, l, false, 0), B, g.n_heads_t, hdt, bf, s);  // keys 0..pos
-    launch_gemv(wo_args(c, w, false), B, EPI_RESID, bf, s);         // h += Wo attn
-    launch_gemv(gu_args(c, w, false), B, EPI_SWIGLU, bf, s);        // SiLU(Wg n) * Wu n
-    launch_gemv(down_args(c, w, false), B, EPI_RESID, bf, s);       // h += Wdown inter
+    GemvArgs wa = wo_args(c, w, false);  // h += Wo attn
+    stat_produce(c, wa, B, false);
+    launch_gemv(wa, B, EPI_RESID, bf, s);
+    GemvArgs ga = gu_args(c, w, false);  // SiLU(Wg n) * Wu n
+    stat_consume(c, ga, B, false, nh);
+    launch_gemv(ga, B, EPI_SWIGLU, bf, s);
+    GemvArgs da = down_args(c, w, false);  // h += Wdown inter
+    stat_produce(c, da, B, false);
+    launch_gemv(da, B, EPI_RESID, bf, s);
   }
   // text head on z = RMSNorm(h), greedy text token
-  launch_gemv(text_head_args(c), B, EPI_STORE, bf, s);
+  GemvArgs ta = text_head_args(c);
+  stat_consume(c, ta, B, false, nh);
+  launch_gemv(ta, B, EPI_STORE, bf, s);
   launch_argmax(argmax_args(c, 0), B, s);
   if (depth) {
     for (int j = 0; j < g.n_q; ++j) {
@@ -546,14 +591,24 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
       a.tok_stride = kSlots;
       a.tok_col = j;
       a.tok_rows = (j == 0 ? g.vocab_text : g.codebook) + 1;
+      stat_consume(c, a, B, false, nh);
+      stat_produce(c, a, B, true);
       launch_gemv(a, B, EPI_EMB, bf, s);
       for (int l = 0; l < g.n_layers_d; ++l) {
         const LayerW& lw = w.layers[l];
-        launch_gemv(qkv_args(c, lw, l, true, j), B, EPI_QKV, bf, s);
+        GemvArgs dq = qkv_args(c, lw, l, true, j);
+        stat_consume(c, dq, B, true, nd);
+        launch_gemv(dq, B, EPI_QKV, bf, s);
         launch_attn_decode(attn_args(c, l, true, j), B, g.n_heads_d, hdd, false, s);
-        launch_gemv(wo_args(c, lw, true), B, EPI_RESID, bf, s);
-        launch_gemv(gu_args(c, lw, true), B, EPI_SWIGLU, bf, s);
-        launch_gemv(down_args(c, lw, true), B, EPI_RESID, bf, s);
+        GemvArgs dwo = wo_args(c, lw, true);
+        stat_produce(c, dwo, B, true);
+        launch_gemv(dwo, B, EPI_RESID, bf, s);
+        GemvArgs dgu = gu_args(c, lw, true);
+        stat_consume(c, dgu, B, true, nd);
+        launch_gemv(dgu, B, EPI_SWIGLU, bf, s);
+        GemvArgs ddn = down_args(c, lw, true);
+        stat_produce(c, ddn, B, true);
+        launch_gemv(ddn, B, EPI_RESID, bf, s);
       }
       GemvArgs hh{};
       hh.eps = g.norm_eps;
@@ -565,6 +620,7 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
       hh.gain = c->at<float>(w.out_norm);
       hh.y = c->at<float>(p.audio_logits) + (long long)j * g.codebook;
       hh.ldy = g.n_q * g.codebook;
+      stat_consume(c, hh, B, true, nd);
       launch_gemv(hh, B, EPI_STORE, bf, s);
       launch_argmax(argmax_args(c, j + 1), B, s);
     }
@@ -1176,26 +1232,39 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
           // time the projection only: the KV append writes into the page of the
           // next free position, which the next step overwrites anyway
           GemvArgs a = qkv_args(c, w, l, false, 0);
+          stat_consume(c, a, batch, false, p.hstat_ld);
           launch_gemv(a, batch, EPI_QKV, p.bf, c->stream);
           bytes = 3 * d * d * e + B * (d * 4 + d * 4 + 2 * d * e);
           break;
         }
-        case MOSHI_KERNEL_WO:
-          launch_gemv(wo_args(c, w, false), batch, EPI_RESID, p.bf, c->stream);
+        case MOSHI_KERNEL_WO: {
+          GemvArgs a = wo_args(c, w, false);
+          stat_produce(c, a, batch, false);
+          launch_gemv(a, batch, EPI_RESID, p.bf, c->stream);
           bytes = d * d * e + B * 3 * d * 4;
           break;
-        case MOSHI_KERNEL_FFN_GATE_UP:
-          launch_gemv(gu_args(c, w, false), batch, EPI_SWIGLU, p.bf, c->stream);
+        }
+        case MOSHI_KERNEL_FFN_GATE_UP: {
+          GemvArgs a = gu_args(c, w, false);
+          stat_consume(c, a, batch, false, p.hstat_ld);
+          launch_gemv(a, batch, EPI_SWIGLU, p.bf, c->stream);
           bytes = 2 * F * d * e + B * (d + F) * 4;
           break;
-        case MOSHI_KERNEL_FFN_DOWN:
-          launch_gemv(down_args(c, w, false), batch, EPI_RESID, p.bf, c->stream);
+        }
+        case MOSHI_KERNEL_FFN_DOWN: {
+          GemvArgs a = down_args(c, w, false);
+          stat_produce(c, a, batch, false);
+          launch_gemv(a, batch, EPI_RESID, p.bf, c->stream);
           bytes = d * F * e + B * (F + 2 * d) * 4;
           break;
-        case MOSHI_KERNEL_TEXT_HEAD:
-          launch_gemv(text_head_args(c), batch, EPI_STORE, p.bf, c->stream);
+        }
+        case MOSHI_KERNEL_TEXT_HEAD: {
+          GemvArgs a = text_head_args(c);
+          stat_consume(c, a, batch, false, p.hstat_ld);
+          launch_gemv(a, batch, EPI_STORE, p.bf, c->stream);
           bytes = g.vocab_text * d * e + B * (d + g.vocab_text) * 4;
           break;
+        }
         case MOSHI_KERNEL_ATTN: {
           // keys 0..pos-1 of the filled cache: read K and V once
           launch_attn_decode(attn_args(c, l, false, 0), batch, g.n_heads_t, g.d_t / g.n_heads_t, p.bf, c->stream);

@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -107,7 +108,12 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, int row0, int n
         const int row = row0 + r;
         if (row + 1 >= N) break;
         const float g = acc[r][b], u = acc[r + 1][b];
-        y[row >> 1] = g / (1.0f + expf(-g)) * u;
+        const float v = g / (1.0f + expf(-g)) * u;
+        y[row >> 1] = v;
+        if (a.y16) {
+          const _Float16 hv = (_Float16)v;
+          a.y16[(long long)b * a.ldy + (row >> 1)] = *(const uint16_t*)&hv;
+        }
       }
     } else if constexpr (EPI == EPI_QKV) {
       const int p = a.pos ? a.pos[b] : a.pos_const;
@@ -390,7 +396,12 @@ __device__ __forceinline__ void pair_store(const GemvArgs& a, float* y, int row,
     y[row] = s0 + p0;
     if (row + 1 < a.N) y[row + 1] = s1 + p1;
   } else if constexpr (EPI == EPI_SWIGLU) {
-    y[row >> 1] = s0 / (1.0f + expf(-s0)) * s1;
+    const float v = s0 / (1.0f + expf(-s0)) * s1;
+    y[row >> 1] = v;
+    if (a.y16) {
+      const _Float16 hv = (_Float16)v;
+      a.y16[(y - a.y) + (row >> 1)] = *(const uint16_t*)&hv;
+    }
   } else if constexpr (EPI == EPI_QKV) {
     const int part = row / a.d;
     const int rr = row - part * a.d;
@@ -769,7 +780,7 @@ __device__ __forceinline__ h16x8 bf8_to_h16x8(u32x4 v) {
 
 constexpr int kMfmaLPG = 8;  // 32-wide K chunks per unit
 
-template <int EPI>
+template <int EPI, bool XG>
 __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int B, int k_begin, int k_end, int SK) {
   constexpr int GROUP = 32 * kMfmaLPG;
   extern __shared__ uint16_t xh[];  // fp16 [B][KP], zero past the chunk
@@ -804,10 +815,12 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
 
   auto grp_of = [&](int set) { return min((blockIdx.x + set * (int)gridDim.x) * RG + rgl, ngroups - 1); };
   u32x4 w[kMfmaLPG];
+  u32x4 xr[XG ? kMfmaLPG : 1];
   auto load_slot = [&](int grp, int g, int i) {
     const int row = min(grp * 16 + tok, N - 1);
     const int k = min(k_begin + g * GROUP + i * 32 + quad * 8, K - 8);
     w[i] = __builtin_nontemporal_load((const u32x4*)(Wb + (long long)row * K + k));
+    if constexpr (XG) xr[i] = *(const u32x4*)(a.x16 + (long long)tk * a.ldx + k);
   };
   if (units > 0) {
 #pragma unroll
@@ -815,7 +828,16 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
   }
 
   // prologue: RMSNorm statistics over the full K, fp16 inputs of [k_begin, k_end) in LDS
-  if (a.gain) {
+  if (!XG && a.gain && a.stat_in) {
+    // from the producer's per-row-group sums of squares, in a fixed order
+    for (int b = wave; b < B; b += kStreamWaves) {
+      float t = 0.f;
+      for (int i = lane; i < a.stat_in_n; i += 64) t += a.stat_in[b * a.stat_in_ld + i];
+      t = wave_sum(t);
+      if (lane == 0) s_rstd[b] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();
+  } else if (!XG && a.gain) {
     float rs[16];
 #pragma unroll
     for (int b = 0; b < 16; ++b) rs[b] = 0.f;
@@ -842,7 +864,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
     }
     __syncthreads();
   }
-  for (int i = tid * 4; i < B * KP; i += 64 * kStreamWaves * 4) {
+  for (int i = tid * 4; i < (XG ? 0 : B * KP); i += 64 * kStreamWaves * 4) {
     const int b = i / KP, k = i - b * KP;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < KC) {
@@ -898,7 +920,14 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
 #pragma unroll
     for (int i = 0; i < kMfmaLPG; ++i) {
       const int k = g * GROUP + i * 32 + quad * 8;
-      u32x4 xv = *(const u32x4*)(xrow + k);
+      u32x4 xv;
+      if constexpr (XG) {
+        xv = xr[i];
+        // chunks past K were read at a clamped address
+        if (k_begin + k >= K) xv = u32x4{0, 0, 0, 0};
+      } else {
+        xv = *(const u32x4*)(xrow + k);
+      }
       if (!tok_live) xv = u32x4{0, 0, 0, 0};
       const h16x8 af = bf8_to_h16x8(w[i]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, *(const h16x8*)&xv, acc, 0, 0, 0);
@@ -921,13 +950,31 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
       }
       const int row = grp * 16 + quad * 4;
       const bool own = (blockIdx.x + set * (int)gridDim.x) * RG + rgl < ngroups;
+      if constexpr (EPI == EPI_RESID || EPI == EPI_EMB) {
+        if (a.stat_out && ks == 0 && own && k_end == K) {
+          // sum of squares of the row group's final outputs (lanes of one token)
+          float sq = 0.f;
+          if (tok_live && row < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float o = acc[r] + pre[r];
+              sq = fmaf(o, o, sq);
+            }
+          }
+          sq += __shfl_xor(sq, 16, 64);
+          sq += __shfl_xor(sq, 32, 64);
+          if (quad == 0 && tok_live) a.stat_out[tok * a.stat_out_ld + grp] = sq;
+        }
+      }
       if (ks == 0 && tok_live && own && row < N) {
         float* y = a.y + (long long)tok * a.ldy;
         const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
         if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
           *(float4*)(y + row) = make_float4(v0 + pre[0], v1 + pre[1], v2 + pre[2], v3 + pre[3]);
         } else if constexpr (EPI == EPI_SWIGLU) {
-          *(float2*)(y + (row >> 1)) = make_float2(v0 / (1.0f + expf(-v0)) * v1, v2 / (1.0f + expf(-v2)) * v3);
+          const float o0 = v0 / (1.0f + expf(-v0)) * v1, o1 = v2 / (1.0f + expf(-v2)) * v3;
+          *(float2*)(y + (row >> 1)) = make_float2(o0, o1);
+          if (a.y16) *(uint32_t*)(a.y16 + (long long)tok * a.ldy + (row >> 1)) = h2pack(o0, o1);
         } else if constexpr (EPI == EPI_QKV) {
           const int part = row / a.d;
           const int rr = row - part * a.d;
@@ -1095,7 +1142,9 @@ static void gemv_mfma_launch(const GemvArgs& a, int B, hipStream_t s) {
   int SK = 1;
   const int ng_launch = (std::min(a.K, (65536 / (2 * B)) / GROUP * GROUP) + GROUP - 1) / GROUP;
   // finest sets (one row group per block) balance the per-CU byte counts best
-  while (SK < kStreamWaves && SK * 2 <= ng_launch) SK *= 2;
+  static int skmax = -1;
+  if (skmax < 0) { const char* e = getenv("MOSHI_SKMAX"); skmax = e ? atoi(e) : kStreamWaves; }
+  while (SK < skmax && SK * 2 <= ng_launch) SK *= 2;
   const int RG = kStreamWaves / SK;
   const int nsets = (ngroups + RG - 1) / RG;
   dim3 grid(std::min(nsets, 2 * device_cus()));
@@ -1106,7 +1155,17 @@ static void gemv_mfma_launch(const GemvArgs& a, int B, hipStream_t s) {
   const int cap = (65536 / (2 * B)) / GROUP * GROUP;
   if (a.K <= cap || EPI != EPI_RESID) {
     const int KP = (a.K + GROUP - 1) / GROUP * GROUP;
-    k_gemv_mfma<EPI><<<grid, T, (size_t)B * KP * 2, s>>>(a, B, 0, a.K, SK);
+    k_gemv_mfma<EPI, false><<<grid, T, (size_t)B * KP * 2, s>>>(a, B, 0, a.K, SK);
+    return;
+  }
+  if (a.x16 && !a.gain) {
+    // one launch that reads the fp16 inputs directly (L2-resident) instead of LDS
+    const int ng_all = (a.K + GROUP - 1) / GROUP;
+    int SKx = 1;
+    while (SKx < kStreamWaves && SKx * 2 <= ng_all) SKx *= 2;
+    const int RGx = kStreamWaves / SKx;
+    const int nsx = (ngroups + RGx - 1) / RGx;
+    k_gemv_mfma<EPI, true><<<dim3(std::min(nsx, 2 * device_cus())), T, 0, s>>>(a, B, 0, a.K, SKx);
     return;
   }
   const int passes = (a.K + cap - 1) / cap;
@@ -1114,8 +1173,12 @@ static void gemv_mfma_launch(const GemvArgs& a, int B, hipStream_t s) {
   for (int k0 = 0; k0 < a.K; k0 += step) {
     const int k1 = std::min(a.K, k0 + step);
     const int KP = (k1 - k0 + GROUP - 1) / GROUP * GROUP;
-    k_gemv_mfma<EPI><<<grid, T, (size_t)B * KP * 2, s>>>(a, B, k0, k1, SK);
+    k_gemv_mfma<EPI, false><<<grid, T, (size_t)B * KP * 2, s>>>(a, B, k0, k1, SK);
   }
+}
+
+static void no_stats(const GemvArgs& a) {
+  if (a.stat_in || a.stat_out) throw std::runtime_error("RMSNorm statistics hand-off needs the batched matrix-core GEMV");
 }
 
 void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s) {
@@ -1134,6 +1197,7 @@ void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s) {
       return;
     }
   }
+  no_stats(a);
   if (bf16)
     gemv_dispatch<true>(a, B, epi, s);
   else
@@ -1450,11 +1514,11 @@ void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, h
 template <bool BF>
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   const int b = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = min(blockIdx.x * 256 + threadIdx.x, a.d - 1);
+  const bool live = blockIdx.x * 256 + threadIdx.x < a.d;
   int t[kStreams];
 #pragma unroll
   for (int k = 0; k < kStreams; ++k) t[k] = a.frames[b * kStreams + k];
-  if (i >= a.d) return;
   float v[kStreams];
 #pragma unroll
   for (int k = 0; k < kStreams; ++k) {
@@ -1469,7 +1533,14 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   float s = 0.f;
 #pragma unroll
   for (int k = 0; k < kStreams; ++k) s += v[k];
-  a.h[(long long)b * a.d + i] = s;
+  if (live) a.h[(long long)b * a.d + i] = s;
+  if (a.stat_out) {
+    __shared__ float red[4];
+    const float sq = wave_sum(live ? s * s : 0.f);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+    __syncthreads();
+    if (threadIdx.x == 0) a.stat_out[b * a.stat_ld + blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
+  }
 }
 
 void launch_embed(const EmbedArgs& a, int B, bool bf16, hipStream_t s) {

@@ -48,6 +48,20 @@ struct GemvArgs {
   KvView kv;
   int kv_bf16;
   int layer;
+  // EPI_SWIGLU: when set, also an fp16 copy of the outputs, [B][ldy]
+  uint16_t* y16;
+  // batched matrix-core path, RMSNorm statistics without re-reading x:
+  // EPI_RESID / EPI_EMB write the sum of squares of each 16-row group of their
+  // final outputs to stat_out[b * stat_out_ld + group]; a normalising launch
+  // takes mean(x^2) from stat_in[b * stat_in_ld + 0 .. stat_in_n - 1], the
+  // partials its producer wrote, added in a fixed order
+  float* stat_out;
+  int stat_out_ld;
+  const float* stat_in;
+  int stat_in_n, stat_in_ld;
+  // batched matrix-core path: fp16 copy of x ([B][ldx], no normalisation)
+  // read directly, for rows too long to stage in LDS
+  const uint16_t* x16;
   // EPI_EMB: y = W x + emb[tok[b * tok_stride + tok_col]]
   const void* emb;
   const int* tok;
@@ -79,6 +93,8 @@ struct EmbedArgs {
   float* h;                // [B][d]
   int d;
   int* err;
+  float* stat_out;         // when set: sum of squares of h[b][256 j .. 256 j + 255] at [b * stat_ld + j]
+  int stat_ld;
 };
 
 struct ArgmaxArgs {

@@ -107,3 +107,57 @@ def test_mid_bf16_teacher_forced_long_ragged():
     for k in ("ce_text", "ce_audio", "ce_total"):
         assert loss[k] == pytest.approx(ref[k], rel=1e-3)
     eng.close()
+
+
+@pytest.mark.parametrize("B", [2, 5])
+def test_mid_bf16_batched_streaming(B):
+    """Batch 2..8 runs the matrix-core GEMVs: RMSNorm statistics handed from the
+    residual writers to the next normalising launch, and the down projection
+    reading its fp16 input directly. Every conversation against its own oracle
+    session, teacher-forced on the oracle's tokens."""
+    from full_duplex_speech_amd import Moshi
+    cfg = config("mid_bf16")
+    w = generate_weights(cfg, seed=0)
+    P, n = 40, 4
+    Vs = [prompt_V(cfg, b, P + n) for b in range(B)]
+    model = Oracle(cfg, w)
+    refs = []
+    for b in range(B):
+        sess = oracle_prefilled(model, Vs[b], P)
+        refs.append([sess.step(Vs[b][P + s, 9:]) for s in range(n)])
+    eng = Moshi(cfg, max_batch=8)
+    eng.load_weights(w)
+    eng.forward_teacher_forced(np.stack([v[:P] for v in Vs]), fill_kv=True, skip_depth=True, logits=False,
+                               loss=False)
+    worst = 0.0
+    for s in range(n):
+        user = np.stack([Vs[b][P + s, 9:] for b in range(B)])
+        force = np.stack([refs[b][s][0] for b in range(B)])
+        tok, glt, gla = eng.step(user, force=force, logits=True)
+        for b in range(B):
+            own, lt, la = refs[b][s]
+            wv, _, _ = compare_frame(cfg, P + s, own, lt, la, tok[b], glt[b], gla[b], TOLS["mid_bf16"])
+            worst = max(worst, wv)
+    eng.close()
+    print(f"mid_bf16 batch {B}: worst rel-L2 {worst:.2e}")
+
+
+def test_mid_teacher_forced_kernel_timer():
+    """moshi_time_kernel times the teacher-forced gate/up GEMM and flash attention
+    at the shape of the last pass and reports their algorithmic FLOPs."""
+    import full_duplex_speech_amd as fds
+    from full_duplex_speech_amd import Moshi
+    cfg = config("mid_bf16")
+    w = generate_weights(cfg, seed=0)
+    B, S = 2, 64
+    V = np.stack([prompt_V(cfg, b, S) for b in range(B)])
+    eng = Moshi(cfg, max_batch=B)
+    eng.load_weights(w)
+    eng.forward_teacher_forced(V, logits=False, loss=True)
+    us, flops = fds.moshi_time_kernel(eng.ctx, "tf_gate_up", B, 2)
+    assert us > 0 and flops == 2.0 * B * S * 2 * cfg.ffn_t * cfg.d_t
+    us, flops = fds.moshi_time_kernel(eng.ctx, "tf_attn", B, 2)
+    assert us > 0 and flops == 4.0 * B * cfg.d_t * S * (S + 1) / 2
+    with pytest.raises(RuntimeError):
+        fds.moshi_time_kernel(eng.ctx, "tf_gate_up", 1, 2)  # batch differs from the pass
+    eng.close()
