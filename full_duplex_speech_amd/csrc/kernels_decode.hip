@@ -483,47 +483,47 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
     for (int i = 0; i < LPG; ++i) load_slot(gw, 0, i, w0[i], w1[i]);
   }
 
-  // prologue: RMSNorm statistics and the normalised, zero-padded inputs in LDS
-  if (a.gain) {
-    float rs[NB];
+  // prologue, one read of x: LDS gets gain * x (zero-padded) and the same pass
+  // sums x^2; the RMSNorm factor 1/sqrt(mean(x^2) + eps) of conversation b is a
+  // scalar of its outputs, applied to the dot products in the epilogue
+  float rs[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) rs[b] = 0.f;
-    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float4 v = *(const float4*)(a.x + (long long)b * a.ldx + k);
-        rs[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      rs[b] = wave_sum(rs[b]);
-      if (lane == 0) s_red[wave][b] = rs[b];
-    }
-    __syncthreads();
-    if (tid < NB) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < kStreamWaves; ++w) t += s_red[w][tid];
-      s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-  }
+  for (int b = 0; b < NB; ++b) rs[b] = 0.f;
   for (int i = tid * 4; i < NB * KP; i += 64 * kStreamWaves * 4) {
     const int b = i / KP, k = i - b * KP;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < K) {
       v = *(const float4*)(a.x + (long long)b * a.ldx + k);
       if (a.gain) {
-        const float r = s_rstd[b];
+        const float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+          if (bb == b) rs[bb] += q;
         const float4 g = *(const float4*)(a.gain + k);
-        v.x *= r * g.x; v.y *= r * g.y; v.z *= r * g.z; v.w *= r * g.w;
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
       }
     }
     xs4[i >> 2] = v;
   }
+  if (a.gain) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      rs[b] = wave_sum(rs[b]);
+      if (lane == 0) s_red[wave][b] = rs[b];
+    }
+  }
+  __syncthreads();
+  if (a.gain && tid < NB) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) t += s_red[w][tid];
+    s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
   __syncthreads();
   if (units == 0) return;
+  float rstd[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) rstd[b] = a.gain ? s_rstd[b] : 1.f;
 
   float acc[2][NB];
 #pragma unroll
@@ -593,15 +593,15 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
       if (lane < NB) {
         // lane b stores conversation b's outputs
         const int b = lane;
-        float s0 = acc[0][0], s1 = acc[1][0], p0 = pre[0][0], p1 = pre[1][0];
+        float s0 = acc[0][0], s1 = acc[1][0], p0 = pre[0][0], p1 = pre[1][0], r = rstd[0];
         int pos = pos_b[0], page = page_b[0];
 #pragma unroll
         for (int bb = 1; bb < NB; ++bb)
           if (bb == b) {
             s0 = acc[0][bb]; s1 = acc[1][bb]; p0 = pre[0][bb]; p1 = pre[1][bb];
-            pos = pos_b[bb]; page = page_b[bb];
+            pos = pos_b[bb]; page = page_b[bb]; r = rstd[bb];
           }
-        pair_store<EPI>(a, a.y + (long long)b * a.ldy, row, s0, s1, p0, p1, pos, page);
+        pair_store<EPI>(a, a.y + (long long)b * a.ldy, row, s0 * r, s1 * r, p0, p1, pos, page);
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r)
@@ -684,38 +684,34 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, i
     p1 = cs[1];
   }
 
-  // RMSNorm statistics and the normalised, zero-padded input in LDS
-  float rstd = 1.f;
-  if (a.gain) {
-    float rs = 0.f;
-    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
-      const float4 v = *(const float4*)(a.x + k);
-      rs += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-    }
-    rs = wave_sum(rs);
-    if (lane == 0) s_red[wave] = rs;
-    __syncthreads();
-    if (tid == 0) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < kStreamWaves; ++w) t += s_red[w];
-      s_rstd = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-    rstd = s_rstd;
-  }
+  // one read of x: LDS gets gain * x (zero-padded) and the same pass sums x^2;
+  // the RMSNorm factor scales the dot products in the epilogue
+  float rs = 0.f;
   for (int k = tid * 4; k < KPAD; k += 64 * kStreamWaves * 4) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < K) {
       v = *(const float4*)(a.x + k);
       if (a.gain) {
+        rs += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
         const float4 g = *(const float4*)(a.gain + k);
-        v.x *= rstd * g.x; v.y *= rstd * g.y; v.z *= rstd * g.z; v.w *= rstd * g.w;
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
       }
     }
     xs4[k >> 2] = v;
   }
+  if (a.gain) {
+    rs = wave_sum(rs);
+    if (lane == 0) s_red[wave] = rs;
+  }
   __syncthreads();
+  if (a.gain && tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) t += s_red[w];
+    s_rstd = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
+  __syncthreads();
+  const float rstd = a.gain ? s_rstd : 1.f;
 
   float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
@@ -748,7 +744,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, i
     t0 += s_part[wave + w][0];
     t1 += s_part[wave + w][1];
   }
-  pair_store<EPI>(a, a.y, pair * 2, t0, t1, p0, p1, pos, page);
+  pair_store<EPI>(a, a.y, pair * 2, t0 * rstd, t1 * rstd, p0, p1, pos, page);
 }
 
 // ---------------------------------------------------------------------------
@@ -827,55 +823,67 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
     for (int i = 0; i < kMfmaLPG; ++i) load_slot(grp_of(0), g_lo, i);
   }
 
-  // prologue: RMSNorm statistics over the full K, fp16 inputs of [k_begin, k_end) in LDS
-  if (!XG && a.gain && a.stat_in) {
-    // from the producer's per-row-group sums of squares, in a fixed order
-    for (int b = wave; b < B; b += kStreamWaves) {
-      float t = 0.f;
-      for (int i = lane; i < a.stat_in_n; i += 64) t += a.stat_in[b * a.stat_in_ld + i];
-      t = wave_sum(t);
-      if (lane == 0) s_rstd[b] = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-  } else if (!XG && a.gain) {
-    float rs[16];
+  // prologue, one read of x: LDS gets fp16(gain * x) of [k_begin, k_end),
+  // zero past the chunk; the RMSNorm factor of each token scales the dot
+  // products in the epilogue. Its statistics come from the producer's partial
+  // sums of squares (stat_in, loaded before the inputs so the two overlap), or
+  // else from the same pass over x (a launch with a gain covers all of K).
+  const bool hand = !XG && a.gain && a.stat_in;
+  float st[2][4];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) rs[b] = 0.f;
-    for (int k = tid * 4; k < K; k += 64 * kStreamWaves * 4) {
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        if (b < B) {
-          const float4 v = *(const float4*)(a.x + (long long)b * a.ldx + k);
-          rs[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int b = wave + h * kStreamWaves, i = lane + 64 * j;
+      st[h][j] = (hand && b < B && i < a.stat_in_n) ? a.stat_in[b * a.stat_in_ld + i] : 0.f;
     }
+  float rs[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      rs[b] = wave_sum(rs[b]);
-      if (lane == 0) s_red[wave][b] = rs[b];
-    }
-    __syncthreads();
-    if (tid < 16) {
-      float t = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < kStreamWaves; ++w2) t += s_red[w2][tid];
-      s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();
-  }
+  for (int b = 0; b < 16; ++b) rs[b] = 0.f;
   for (int i = tid * 4; i < (XG ? 0 : B * KP); i += 64 * kStreamWaves * 4) {
     const int b = i / KP, k = i - b * KP;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (k < KC) {
       v = *(const float4*)(a.x + (long long)b * a.ldx + k_begin + k);
       if (a.gain) {
-        const float r = s_rstd[b];
+        if (!hand) {
+          const float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+          for (int bb = 0; bb < 16; ++bb)
+            if (bb == b) rs[bb] += q;
+        }
         const float4 g = *(const float4*)(a.gain + k_begin + k);
-        v.x *= r * g.x; v.y *= r * g.y; v.z *= r * g.z; v.w *= r * g.w;
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
       }
     }
     *(uint2*)(xh + i) = make_uint2(h2pack(v.x, v.y), h2pack(v.z, v.w));
+  }
+  if (hand) {
+    // partials in a fixed order: lane-strided sums, then the wave reduction
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = wave + h * kStreamWaves;
+      float t = (st[h][0] + st[h][1]) + (st[h][2] + st[h][3]);
+      for (int i = lane + 256; i < a.stat_in_n; i += 64)
+        if (b < B) t += a.stat_in[b * a.stat_in_ld + i];
+      t = wave_sum(t);
+      if (lane == 0 && b < B) s_rstd[b] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+  } else if (!XG && a.gain) {
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      if (b < B) {
+        rs[b] = wave_sum(rs[b]);
+        if (lane == 0) s_red[wave][b] = rs[b];
+      }
+    }
+  }
+  __syncthreads();
+  if (!XG && a.gain && !hand && tid < B) {
+    float t = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kStreamWaves; ++w2) t += s_red[w2][tid];
+    s_rstd[tid] = 1.0f / sqrtf(t / (float)K + a.eps);
   }
   __syncthreads();
   if (my_sets == 0) return;
@@ -903,6 +911,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
   float pre[4], pre_n[4];
   load_pre(grp_of(0), pre);
   f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  const float rnorm = (!XG && a.gain) ? s_rstd[tk] : 1.f;  // this lane's token
   const uint16_t* xrow = xh + (long long)tk * KP;
   const bool tok_live = tok < B;
 
@@ -957,7 +966,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
           if (tok_live && row < N) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float o = acc[r] + pre[r];
+              const float o = acc[r] * rnorm + pre[r];  // the stored output
               sq = fmaf(o, o, sq);
             }
           }
@@ -968,7 +977,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_mfma(GemvArgs a, int
       }
       if (ks == 0 && tok_live && own && row < N) {
         float* y = a.y + (long long)tok * a.ldy;
-        const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];
+        const float v0 = acc[0] * rnorm, v1 = acc[1] * rnorm, v2 = acc[2] * rnorm, v3 = acc[3] * rnorm;
         if constexpr (EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_EMB) {
           *(float4*)(y + row) = make_float4(v0 + pre[0], v1 + pre[1], v2 + pre[2], v3 + pre[3]);
         } else if constexpr (EPI == EPI_SWIGLU) {
