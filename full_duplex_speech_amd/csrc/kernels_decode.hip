@@ -1471,7 +1471,53 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a, int NS) {
   a.out[(long long)b * a.ldo + h * HD + t] = o / L;
 }
 
+// Depth attention: at most kDepthAttnKeys keys of this frame's positions
+// (fp32 cache), one wave per (head, conversation), lane = head dimension
+// (hd <= 64). q, K and V are requested together, so the kernel waits on
+// memory once; softmax with max subtraction.
+constexpr int kDepthAttnKeys = 8;
+
+__global__ __launch_bounds__(64) void k_attn_depth(AttnArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  const int hd = a.kv.hd;
+  const bool on = lane < hd;
+  const int dim = on ? lane : 0;
+  const int P = (a.pos ? a.pos[b] : a.pos_const) + 1;
+  const float* kvb = (const float*)a.kv.base;
+  const long long kb = a.kv.offset(b, a.layer, 0, h, 0) + dim;
+  const long long vb = a.kv.offset(b, a.layer, 1, h, 0) + dim;
+  const float q = a.q[(long long)b * a.ldq + h * hd + dim] * a.scale;
+  float kk[kDepthAttnKeys], vv[kDepthAttnKeys];
+#pragma unroll
+  for (int t = 0; t < kDepthAttnKeys; ++t) {
+    const int tt = min(t, P - 1);
+    kk[t] = kvb[kb + (long long)tt * hd];
+    vv[t] = kvb[vb + (long long)tt * hd];
+  }
+  float sc[kDepthAttnKeys], m = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < kDepthAttnKeys; ++t) {
+    sc[t] = wave_sum(on ? q * kk[t] : 0.f);
+    if (t < P) m = fmaxf(m, sc[t]);
+  }
+  float l = 0.f, o = 0.f;
+#pragma unroll
+  for (int t = 0; t < kDepthAttnKeys; ++t) {
+    if (t < P) {
+      const float pr = expf(sc[t] - m);
+      l += pr;
+      o = fmaf(pr, vv[t], o);
+    }
+  }
+  if (on) a.out[(long long)b * a.ldo + h * hd + dim] = o / l;
+}
+
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s) {
+  if (!a.kv.page_table && !a.pos && !kv_bf16 && a.pos_const < kDepthAttnKeys && a.pos_const < a.kv.pf &&
+      hd <= 64 && a.kv.hd == hd) {
+    k_attn_depth<<<dim3(H, B), 64, 0, s>>>(a);
+    return;
+  }
   if (a.kv.page_table && a.pos) {
     // temporal cache: about half a block per CU over (split, head, conversation);
     // at batch 1 and ~500 keys, 4 splits of 32 heads beat 8 (4.11 vs 4.16 ms per
