@@ -70,8 +70,8 @@ __device__ __forceinline__ u32x4t bf8_to_h8(u32x4t v) {
 // ---------------------------------------------------------------------------
 constexpr int kTM = 128;
 
-template <int EPI, int WT, int kTK>
-__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
+template <int EPI, int WT, int kTK, int PD>
+__global__ __launch_bounds__(256, 2) void k_gemm_bf16(GemmArgs g) {
   constexpr int kTN = 64 * WT;
   constexpr int kLdsRow = kTK + 8;        // padded row (fp16)
   constexpr int CPRW = kTK / 8;           // 16-byte chunks per row and K step
@@ -162,6 +162,20 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
 
   // nk is even (K % (2 kTK) == 0): the loop body is two steps and has no exits;
   // the last stores write re-read data that nothing reads
+  if constexpr (PD == 1) {
+    // one register set: the loads of step kt + 1 are issued before step kt is
+    // computed (the last iteration re-reads the last step into an unused buffer)
+    gload(ra, 0);
+    lstore(ra, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      gload(ra, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(kt & 1);
+      lstore(ra, (kt & 1) ^ 1);
+      __syncthreads();
+    }
+  } else {
   gload(ra, 0);
   gload(rb, 1);
   lstore(ra, 0);
@@ -179,6 +193,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs g) {
     compute(1);
     lstore(ra, 0);
     __syncthreads();
+  }
   }
 
   // epilogue: lane holds token m = m0 + wm*64 + j*32 + lane%32 and features
@@ -262,25 +277,25 @@ void launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, long long n, hipStre
   k_bf16_to_f16<<<(unsigned)blocks, 256, 0, s>>>(src, dst, n);
 }
 
-template <int WT, int KT>
+template <int WT, int KT, int PD>
 static void gemm_launch(const GemmArgs& g, int epi, hipStream_t s) {
   const int tiles = ((g.N + 64 * WT - 1) / (64 * WT)) * ((g.M + kTM - 1) / kTM);
   switch (epi) {
-    case TF_STORE_F32: k_gemm_bf16<TF_STORE_F32, WT, KT><<<tiles, 256, 0, s>>>(g); break;
-    case TF_RESID: k_gemm_bf16<TF_RESID, WT, KT><<<tiles, 256, 0, s>>>(g); break;
-    case TF_EMB: k_gemm_bf16<TF_EMB, WT, KT><<<tiles, 256, 0, s>>>(g); break;
-    case TF_SWIGLU: k_gemm_bf16<TF_SWIGLU, WT, KT><<<tiles, 256, 0, s>>>(g); break;
-    case TF_QKV: k_gemm_bf16<TF_QKV, WT, KT><<<tiles, 256, 0, s>>>(g); break;
+    case TF_STORE_F32: k_gemm_bf16<TF_STORE_F32, WT, KT, PD><<<tiles, 256, 0, s>>>(g); break;
+    case TF_RESID: k_gemm_bf16<TF_RESID, WT, KT, PD><<<tiles, 256, 0, s>>>(g); break;
+    case TF_EMB: k_gemm_bf16<TF_EMB, WT, KT, PD><<<tiles, 256, 0, s>>>(g); break;
+    case TF_SWIGLU: k_gemm_bf16<TF_SWIGLU, WT, KT, PD><<<tiles, 256, 0, s>>>(g); break;
+    case TF_QKV: k_gemm_bf16<TF_QKV, WT, KT, PD><<<tiles, 256, 0, s>>>(g); break;
   }
 }
 
 void launch_gemm_bf16(const GemmArgs& g, int epi, hipStream_t s) {
   if (g.K % 64 != 0 || g.K <= 0) throw std::runtime_error("teacher-forced GEMM needs K % 64 == 0");
-  // 64-wide K steps need an even number of them
+  // 64-wide K steps with two register sets need an even number of them
   if (g.K % 128 == 0)
-    gemm_launch<2, 64>(g, epi, s);
+    gemm_launch<2, 64, 2>(g, epi, s);
   else
-    gemm_launch<2, 32>(g, epi, s);
+    gemm_launch<2, 32, 2>(g, epi, s);
 }
 
 // ---------------------------------------------------------------------------
