@@ -229,7 +229,7 @@ Plan make_plan(const moshi_config& c) {
   // matrix-core pass: bf16 weights, GEMM K dims multiple of 32, head dims the
   // flash/depth attention kernels support
   p.tf_mfma = p.bf && d % 32 == 0 && F % 32 == 0 && dd % 32 == 0 && Fd % 32 == 0 && (hdt == 64 || hdt == 128) &&
-              hdd <= 64;
+              (hdd == 16 || hdd == 32 || hdd == 64);
   if (p.tf_mfma) {
     const size_t T = (size_t)tf;
     p.w16 = p.take(p.meta_row0);

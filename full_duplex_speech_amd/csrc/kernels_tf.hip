@@ -569,40 +569,71 @@ void launch_flash_attn(const FlashArgs& f, int B, int H, int hd, hipStream_t s) 
 // h attends to positions 0..j of the same frame (at most 8). One wave per
 // (m, head); q, k, v are bf16 [position][M][d] buffers.
 // ---------------------------------------------------------------------------
+// HD / 8 lanes per (m, head) item, 8 fp16 per lane; q, K and V of the j+1
+// positions are requested together (positions past j re-read position j)
+template <int HD>
 __global__ __launch_bounds__(256) void k_depth_attn(DepthAttnArgs a) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long item = (long long)blockIdx.x * 4 + wave;  // (m, head)
-  const long long m = item / a.H;
-  const int h = (int)(item - m * a.H);
-  if (m >= a.M) return;
-  const int hd = a.hd;  // 64: one element per lane
+  constexpr int LPI = HD / 8, IPW = 64 / LPI;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, li = lane % LPI;
+  const long long item = ((long long)blockIdx.x * 4 + wave) * IPW + lane / LPI;  // (m, head)
+  const long long m = min(item / a.H, a.M - 1);
+  const int h = (int)(item % a.H);
   const int j = a.j;
-  const float qv = lane < hd ? tf_h2f(a.q[((long long)j * a.M + m) * a.d + h * hd + lane]) : 0.f;
-  float sc[8];
-  float mx = -INFINITY;
+  const long long col = (long long)h * HD + li * 8;
+  const u32x4t qr = *(const u32x4t*)(a.q + ((long long)j * a.M + m) * a.d + col);
+  u32x4t kr[8], vr[8];
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    if (p > j) break;
-    float v = lane < hd ? qv * tf_h2f(a.k[((long long)p * a.M + m) * a.d + h * hd + lane]) : 0.f;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    sc[p] = v * a.scale;
-    mx = fmaxf(mx, sc[p]);
+    const long long off = ((long long)min(p, j) * a.M + m) * a.d + col;
+    kr[p] = *(const u32x4t*)(a.k + off);
+    vr[p] = *(const u32x4t*)(a.v + off);
   }
-  float l = 0.f, o = 0.f;
+  float qf[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qf[e] = tf_h2f((uint16_t)(qr[e >> 1] >> (16 * (e & 1))));
+  float sc[8], mx = -INFINITY;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    if (p > j) break;
-    const float w = expf(sc[p] - mx);
-    l += w;
-    if (lane < hd) o = fmaf(w, tf_h2f(a.v[((long long)p * a.M + m) * a.d + h * hd + lane]), o);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d = fmaf(qf[e], tf_h2f((uint16_t)(kr[p][e >> 1] >> (16 * (e & 1)))), d);
+#pragma unroll
+    for (int o = LPI / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+    sc[p] = d * a.scale;
+    if (p <= j) mx = fmaxf(mx, sc[p]);
   }
-  if (lane < hd) a.out[m * a.d + h * hd + lane] = tf_f2h(o / l);
+  float l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (p <= j) {
+      const float w = expf(sc[p] - mx);
+      l += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = fmaf(w, tf_h2f((uint16_t)(vr[p][e >> 1] >> (16 * (e & 1)))), o[e]);
+    }
+  }
+  if (item >= (long long)a.M * a.H) return;
+  const float inv = 1.f / l;
+  u32x4t out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    out[e] = (uint32_t)tf_f2h(o[2 * e] * inv) | ((uint32_t)tf_f2h(o[2 * e + 1] * inv) << 16);
+  *(u32x4t*)(a.out + m * a.d + col) = out;
 }
 
 void launch_depth_attn(const DepthAttnArgs& a, hipStream_t s) {
   const long long items = (long long)a.M * a.H;
-  k_depth_attn<<<(unsigned)((items + 3) / 4), 256, 0, s>>>(a);
+  if (a.hd == 64) {
+    k_depth_attn<64><<<(unsigned)((items + 31) / 32), 256, 0, s>>>(a);
+  } else if (a.hd == 32) {
+    k_depth_attn<32><<<(unsigned)((items + 63) / 64), 256, 0, s>>>(a);
+  } else if (a.hd == 16) {
+    k_depth_attn<16><<<(unsigned)((items + 127) / 128), 256, 0, s>>>(a);
+  } else {
+    throw std::runtime_error("teacher-forced depth attention supports head dims 16, 32 and 64");
+  }
 }
 
 // ---------------------------------------------------------------------------
