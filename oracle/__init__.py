@@ -17,3 +17,4 @@ from .moshi_oracle import (  # noqa: F401
     top2_margin,
     undelay_codes,
 )
+from .quant import dequantize_q8, dequantized_weights, is_linear, quantize_q8  # noqa: F401,E402

@@ -55,7 +55,7 @@ class MoshiConfig:
     delay: int = 1
     rope_base: float = 10000.0
     norm_eps: float = 1e-5
-    dtype: str = "f32"  # weight precision: "f32" or "bf16"
+    dtype: str = "f32"  # weight precision: "f32", "bf16" or "q8" (8-bit blocks of the bf16 values)
     # workload
     batch: int = 1
     prompt_frames: int = 0
@@ -100,6 +100,14 @@ CONFIGS: Dict[str, MoshiConfig] = {
     # 7B shape, batch 1: 375-frame prompt then 250 greedy frames
     "b1_7b": MoshiConfig(
         name="b1_7b", vocab_text=32000, dtype="bf16", batch=1, prompt_frames=375,
+        gen_frames=250, **_TEMPORAL_7B, **_DEPTH_7B),
+    # the same model with its linear maps in 8-bit blocks (quantised from the bf16 values)
+    "mid_q8": MoshiConfig(
+        name="mid_q8", d_t=1024, n_layers_t=8, n_heads_t=16, ffn_t=2816, ctx_max=4096,
+        vocab_text=32000, dtype="q8", batch=1, prompt_frames=375, gen_frames=125,
+        **_DEPTH_7B),
+    "b1_7b_q8": MoshiConfig(
+        name="b1_7b_q8", vocab_text=32000, dtype="q8", batch=1, prompt_frames=375,
         gen_frames=250, **_TEMPORAL_7B, **_DEPTH_7B),
     # 7B shape, 8 conversations at 5-minute context
     "b8_7b_5min": MoshiConfig(
@@ -184,7 +192,7 @@ def _draw(shape, init, seed, ordinal, dtype) -> np.ndarray:
         return np.ones(shape, dtype=np.float32)
     a = np.random.default_rng([seed, ordinal]).standard_normal(shape, dtype=np.float32)
     a *= np.float32(LINEAR_STD if init == "linear" else EMBED_STD)
-    if dtype == "bf16":
+    if dtype in ("bf16", "q8"):
         bf16_round(a)
     return a
 
