@@ -5,7 +5,7 @@ prompt prefilled into the KV cache, then 250 greedy frames with new random user
 codes every frame. Prints one JSON line (frames/s, ms per frame, roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample).
 
-    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|mid_bf16|tiny]
+    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|mid_bf16|tiny]
 """
 from __future__ import annotations
 
@@ -72,8 +72,10 @@ def joint_prompt(fds, cfg, b, n_frames, seed=0):
 def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
     """The oracle (float32) on the host: prefill untimed, then `frames` greedy frames
     of conversation 0 timed."""
-    from oracle import Oracle, Session
+    from oracle import Oracle, Session, dequantized_weights
     cores = len(os.sched_getaffinity(0))
+    if cfg.dtype == "q8":  # the 8-bit model computes with the quantise-dequantise image of its linear maps
+        weights = dequantized_weights(weights)
     m = Oracle(cfg, weights, dtype=np.float32)
     sess = Session(m)
     t0 = time.perf_counter()
@@ -183,7 +185,8 @@ def main():
         dt = time.perf_counter() - t0
         frames_per_step = B
         log(f"{K} steps of {B} frame(s): {dt * 1000 / K:.3f} ms/step; last tokens {out_dev[K - 1, 0].tolist()}")
-        workload = {"workload": f"7B-shape streaming decode, batch {B}, {P}-frame prompt then {K} greedy frames"
+        shape = "7B-shape, 8-bit block weights" if cfg.dtype == "q8" else "7B-shape"
+        workload = {"workload": f"{shape} streaming decode, batch {B}, {P}-frame prompt then {K} greedy frames"
                     if cfg.d_t == 4096 else f"{cfg.name} streaming decode, batch {B}, {P}-frame prompt then "
                     f"{K} greedy frames", "config": cfg.name, "batch": B, "prompt_frames": P, "frames": K}
 
@@ -213,7 +216,8 @@ def main():
         traffic = measured_traffic() if (cfg.name == "b1_7b" and B == 1) else None
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": "k_gemv (RMSNorm + gate/up + SiLU product, one temporal layer)",
+                    "kernel": ("k_gemv_q8" if cfg.dtype == "q8" else "k_gemv") +
+                              " (RMSNorm + gate/up + SiLU product, one temporal layer)",
                     "bytes_per_launch": nbytes, "us_per_launch": round(us, 3)}
         others = {}
         for kname in ("qkv", "wo", "ffn_down", "text_head", "attn"):
@@ -221,12 +225,14 @@ def main():
             others[kname] = {"us": round(kus, 2), "GB/s": round(kb / (kus * 1e-6) / 1e9, 1)}
         roofline["other_kernels"] = others
         # whole-frame algorithmic bytes: every weight once + K/V read at the mean context
-        esz = 2 if cfg.dtype == "bf16" else 4
+        # (8-bit linear maps: one code byte plus 4 bytes of fp16 scale and min per 32 weights)
+        esz = 2 if cfg.dtype in ("bf16", "q8") else 4
+        lin_esz = 1.125 if cfg.dtype == "q8" else esz
         lin = param_count(cfg) - (cfg.vocab_text + 1 + 16 * (cfg.codebook + 1)) * cfg.d_t \
             - (cfg.vocab_text + 1 + 7 * (cfg.codebook + 1)) * cfg.d_d
         mean_ctx = P + (K + 1) / 2
         kv = B * cfg.n_layers_t * 2 * cfg.d_t * esz * mean_ctx
-        frame_bytes = lin * esz + kv
+        frame_bytes = lin * lin_esz + kv
         roofline["frame_bytes_per_step"] = frame_bytes
         roofline["frame_frac"] = round(frame_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
@@ -248,7 +254,7 @@ def main():
         "metric": "RQ-Transformer frames/sec and ms/frame at batch 1 and 8 (7B shape, bf16)",
         "value": round(value, 3), "unit": "frames/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": cfg.dtype if cfg.dtype == "bf16" else "f32",
+        "vs_baseline": None, "dtype": cfg.dtype if cfg.dtype in ("bf16", "q8") else "f32",
         "data": "synthetic (seeded random-init weights, uniform random tokens)",
         "config": workload, "roofline": roofline, "cpu_baseline": cpu,
         "host": {"cpu": platform.processor() or platform.machine(), "cores": len(os.sched_getaffinity(0))},

@@ -22,6 +22,7 @@ MOSHI_EHIP = -4
 MOSHI_ESTATE = -5
 MOSHI_F32 = 0
 MOSHI_BF16 = 1
+MOSHI_Q8 = 2
 MOSHI_DEVICE_PTRS = 1
 MOSHI_TF_FILL_KV = 2
 MOSHI_TF_SKIP_DEPTH = 4
@@ -56,7 +57,7 @@ class moshi_loss(ctypes.Structure):
 EXPORTS = (
     "moshi_workspace_bytes", "moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset",
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
-    "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel",
+    "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel", "moshi_read_q8",
 )
 KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5, "tf_gate_up": 6,
            "tf_attn": 7}
@@ -88,11 +89,12 @@ def lib() -> ctypes.CDLL:
     L.moshi_last_error.argtypes = [VP]
     L.moshi_last_error.restype = ctypes.c_char_p
     L.moshi_time_kernel.argtypes = [VP, I32, I32, I32, P(ctypes.c_float), P(ctypes.c_double)]
+    L.moshi_read_q8.argtypes = [VP, ctypes.c_char_p, VP, VP, VP]
     L.moshi_destroy.argtypes = [VP]
     L.moshi_destroy.restype = None
     for n in ("moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset", "moshi_step",
               "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
-              "moshi_undelay_codes", "moshi_time_kernel"):
+              "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -128,7 +130,7 @@ def config_struct(cfg, max_batch: Optional[int] = None, page_frames: int = 64, n
         setattr(c, n, int(getattr(cfg, n)))
     c.rope_base = float(cfg.rope_base)
     c.norm_eps = float(cfg.norm_eps)
-    c.dtype = MOSHI_BF16 if cfg.dtype == "bf16" else MOSHI_F32
+    c.dtype = {"bf16": MOSHI_BF16, "q8": MOSHI_Q8}.get(cfg.dtype, MOSHI_F32)
     c.max_batch = int(max_batch if max_batch is not None else cfg.batch)
     c.page_frames = page_frames
     c.n_pages = n_pages
@@ -218,6 +220,16 @@ def moshi_time_kernel(ctx, kernel: str, batch: int, iters: int) -> Tuple[float, 
     nbytes = ctypes.c_double()
     _check(ctx, lib().moshi_time_kernel(ctx, KERNELS[kernel], batch, iters, ctypes.byref(us), ctypes.byref(nbytes)))
     return float(us.value), float(nbytes.value)
+
+
+def moshi_read_q8(ctx, name: str, rows: int, cols: int):
+    """(codes uint8 [rows, cols], scale float16 [rows, cols/32], min float16 [rows, cols/32]) of an
+    8-bit model's linear tensor, as stored on the device."""
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scale = np.empty((rows, cols // 32), dtype=np.uint16)
+    mn = np.empty((rows, cols // 32), dtype=np.uint16)
+    _check(ctx, lib().moshi_read_q8(ctx, name.encode(), codes.ctypes.data, scale.ctypes.data, mn.ctypes.data))
+    return codes, scale.view(np.float16), mn.view(np.float16)
 
 
 def moshi_last_error(ctx) -> str:

@@ -12,6 +12,7 @@
 #include <functional>
 #include <map>
 #include <string>
+#include <thread>
 #include <utility>
 #include <vector>
 
@@ -58,11 +59,17 @@ struct Dest {
   long long mult, add;
   bool f32;        // stored as float32 regardless of dtype
   bool loaded;
+  bool linear;     // a linear map (8-bit blocks in MOSHI_Q8 models)
 };
 
 struct Plan {
   bool bf = false;
+  bool q8 = false;  // linear maps in 8-bit blocks (embeddings and KV bf16)
   int esz = 4;
+  // 8-bit blocks: the codes of the bf16-layout element at byte offset o sit at
+  // q8w + o/2, its block's parameters at q8p + o/16
+  size_t q8w = 0, q8p = 0;
+  size_t wbytes = 0;  // bytes of the weight region (offset 0)
   size_t total = 0;
   size_t take(size_t bytes) {
     size_t o = (total + 255) & ~(size_t)255;
@@ -119,7 +126,11 @@ int validate(const moshi_config& c, std::string& msg) {
   if (c.vocab_text < 2 || c.codebook < 2) return bad("vocabularies must have at least 2 entries");
   if (c.delay < 0) return bad("delay must be >= 0");
   if (!(c.rope_base > 0.f) || !(c.norm_eps > 0.f)) return bad("rope_base and norm_eps must be positive");
-  if (c.dtype != MOSHI_F32 && c.dtype != MOSHI_BF16) return bad("dtype must be MOSHI_F32 or MOSHI_BF16");
+  if (c.dtype != MOSHI_F32 && c.dtype != MOSHI_BF16 && c.dtype != MOSHI_Q8)
+    return bad("dtype must be MOSHI_F32, MOSHI_BF16 or MOSHI_Q8");
+  if (c.dtype == MOSHI_Q8 && c.max_batch != 1) return bad("MOSHI_Q8 weights stream one conversation: max_batch must be 1");
+  if (c.dtype == MOSHI_Q8 && (c.d_t % 32 || c.d_d % 32 || c.ffn_t % 32 || c.ffn_d % 32))
+    return bad("MOSHI_Q8 needs every linear input width to be a multiple of 32");
   if (c.max_batch < 1 || c.max_batch > kMaxBatch) return bad("max_batch must be in 1..8");
   if (c.page_frames != 8 && c.page_frames != 16 && c.page_frames != 32 && c.page_frames != 64)
     return bad("page_frames must be 8, 16, 32 or 64");
@@ -131,7 +142,8 @@ int validate(const moshi_config& c, std::string& msg) {
 
 Plan make_plan(const moshi_config& c) {
   Plan p;
-  p.bf = c.dtype == MOSHI_BF16;
+  p.bf = c.dtype == MOSHI_BF16 || c.dtype == MOSHI_Q8;
+  p.q8 = c.dtype == MOSHI_Q8;
   p.esz = p.bf ? 2 : 4;
   const size_t e = p.esz;
   const long long d = c.d_t, F = c.ffn_t, dd = c.d_d, Fd = c.ffn_d;
@@ -171,6 +183,11 @@ Plan make_plan(const moshi_config& c) {
     w.out_norm = p.take(dd * 4);
     w.head = p.take((long long)c.codebook * dd * e);
     p.dj.push_back(w);
+  }
+  p.wbytes = p.total;  // the weight region [0, wbytes)
+  if (p.q8) {
+    p.q8w = p.take(p.wbytes / 2);
+    p.q8p = p.take(p.wbytes / 16);
   }
   p.meta_row0 = p.take(kStreams * 8);
   p.meta_rows = p.take(kStreams * 4);
@@ -232,7 +249,7 @@ Plan make_plan(const moshi_config& c) {
               (hdd == 16 || hdd == 32 || hdd == 64);
   if (p.tf_mfma) {
     const size_t T = (size_t)tf;
-    p.w16 = p.take(p.meta_row0);
+    p.w16 = p.take(p.wbytes);
     p.tf_H = p.take(T * d * 4);
     p.tf_Xn = p.take(T * d * 2);
     p.tf_I = p.take(T * F * 2);
@@ -295,7 +312,11 @@ namespace {
 
 void add_dest(moshi_ctx* c, const std::string& name, size_t off, long long rows, int cols, long long mult = 1,
               long long add = 0, bool f32 = false) {
-  c->dests[name] = Dest{off, rows, cols, mult, add, f32, false};
+  static const char* kLinear[] = {"wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "text_head", "in_proj", "head"};
+  const std::string last = name.substr(name.rfind('.') + 1);
+  bool lin = false;
+  for (const char* l : kLinear) lin = lin || last == l;
+  c->dests[name] = Dest{off, rows, cols, mult, add, f32, false, lin};
 }
 
 void build_dests(moshi_ctx* c) {
@@ -372,13 +393,25 @@ KvView depth_kv(moshi_ctx* c) {
 
 // Argument builders of the frame's kernels (shared by the frame sequence and
 // the kernel timer).
+// weights of a streaming GEMV: the bf16/fp32 matrix at byte offset off, or its
+// 8-bit codes and block parameters in MOSHI_Q8 models
+void set_weights(moshi_ctx* c, GemvArgs& a, size_t off) {
+  const Plan& p = c->plan;
+  if (p.q8) {
+    a.W = c->ws + p.q8w + off / 2;
+    a.Wq8p = c->at<uint32_t>(p.q8p + off / 16);
+  } else {
+    a.W = c->ws + off;
+  }
+}
+
 GemvArgs qkv_args(moshi_ctx* c, const LayerW& w, int layer, bool depth_model, int pos_const) {
   const moshi_config& g = c->cfg;
   const Plan& p = c->plan;
   const int D = depth_model ? g.d_d : g.d_t;
   GemvArgs a{};
   a.eps = g.norm_eps;
-  a.W = c->ws + w.wqkv;
+  set_weights(c, a, w.wqkv);
   a.N = 3 * D;
   a.K = D;
   a.x = c->at<float>(depth_model ? p.hd : p.h);
@@ -423,7 +456,7 @@ GemvArgs wo_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
   const Plan& p = c->plan;
   const int D = depth_model ? c->cfg.d_d : c->cfg.d_t;
   GemvArgs o{};
-  o.W = c->ws + w.wo;
+  set_weights(c, o, w.wo);
   o.N = D;
   o.K = D;
   o.x = c->at<float>(depth_model ? p.dattn : p.attn);
@@ -439,7 +472,7 @@ GemvArgs gu_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
   const int D = depth_model ? g.d_d : g.d_t, F = depth_model ? g.ffn_d : g.ffn_t;
   GemvArgs f{};
   f.eps = g.norm_eps;
-  f.W = c->ws + w.wgu;
+  set_weights(c, f, w.wgu);
   f.N = 2 * F;
   f.K = D;
   f.x = c->at<float>(depth_model ? p.hd : p.h);
@@ -456,7 +489,7 @@ GemvArgs down_args(moshi_ctx* c, const LayerW& w, bool depth_model) {
   const Plan& p = c->plan;
   const int D = depth_model ? g.d_d : g.d_t, F = depth_model ? g.ffn_d : g.ffn_t;
   GemvArgs dn{};
-  dn.W = c->ws + w.wdown;
+  set_weights(c, dn, w.wdown);
   dn.N = D;
   dn.K = F;
   dn.x = c->at<float>(depth_model ? p.dinter : p.inter);
@@ -472,7 +505,7 @@ GemvArgs text_head_args(moshi_ctx* c) {
   const Plan& p = c->plan;
   GemvArgs a{};
   a.eps = g.norm_eps;
-  a.W = c->ws + p.text_head;
+  set_weights(c, a, p.text_head);
   a.N = g.vocab_text;
   a.K = g.d_t;
   a.x = c->at<float>(p.h);
@@ -578,7 +611,7 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
       // u_j = W_in^j z + E_D^j[token of slot j]
       GemvArgs a{};
       a.eps = g.norm_eps;
-      a.W = c->ws + w.in_proj;
+      set_weights(c, a, w.in_proj);
       a.N = g.d_d;
       a.K = g.d_t;
       a.x = c->at<float>(p.h);
@@ -612,7 +645,7 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
       }
       GemvArgs hh{};
       hh.eps = g.norm_eps;
-      hh.W = c->ws + w.head;
+      set_weights(c, hh, w.head);
       hh.N = g.codebook;
       hh.K = g.d_d;
       hh.x = c->at<float>(p.hd);
@@ -995,6 +1028,93 @@ int moshi_create(const moshi_config* cfg, void* hip_stream, void* workspace, siz
   return MOSHI_OK;
 }
 
+// 8-bit block format of a linear map (the walkthrough's "压缩Moshi及其对语音质量的
+// 影响" section, "量化格式": asymmetric MinMax over blocks; block 32 and float16
+// parameters per its Table 10 caption). Host code, float32 IEEE arithmetic:
+// the weight is first rounded to bf16 (the model's precision), then per block
+// scale = (max - min) / 255 and min are rounded to float16 and
+// q = clamp(round_half_even((w - min16) / scale16), 0, 255); a flat block
+// stores scale 0 and q = 0. Packs (scale | min << 16).
+static uint16_t f32_to_f16_bits(float f) {
+  const _Float16 h = (_Float16)f;
+  uint16_t u;
+  memcpy(&u, &h, 2);
+  return u;
+}
+static float f16_bits_to_f32(uint16_t u) {
+  _Float16 h;
+  memcpy(&h, &u, 2);
+  return (float)h;
+}
+static float bf16_round_host(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  u &= 0xffff0000u;
+  float r;
+  memcpy(&r, &u, 4);
+  return r;
+}
+static void quantize_rows_q8(const float* src, long long rows, int cols, uint8_t* q, uint32_t* prm) {
+  const int nb = cols / 32;
+  auto work = [&](long long r_lo, long long r_hi) {
+    float b[32];
+    for (long long r = r_lo; r < r_hi; ++r) {
+      for (int k = 0; k < nb; ++k) {
+        const float* w = src + r * cols + k * 32;
+        for (int i = 0; i < 32; ++i) b[i] = bf16_round_host(w[i]);
+        float mn = b[0], mx = b[0];
+        for (int i = 1; i < 32; ++i) {
+          mn = std::min(mn, b[i]);
+          mx = std::max(mx, b[i]);
+        }
+        const uint16_t s16 = f32_to_f16_bits((mx - mn) / 255.0f);
+        const uint16_t m16 = f32_to_f16_bits(mn);
+        const float sc = f16_bits_to_f32(s16), m = f16_bits_to_f32(m16);
+        uint8_t* qo = q + r * cols + k * 32;
+        for (int i = 0; i < 32; ++i) {
+          float v = sc > 0.f ? nearbyintf((b[i] - m) / sc) : 0.f;
+          v = std::min(255.f, std::max(0.f, v));
+          qo[i] = (uint8_t)v;
+        }
+        prm[r * nb + k] = (uint32_t)s16 | ((uint32_t)m16 << 16);
+      }
+    }
+  };
+  const int nt = (int)std::max<long long>(1, std::min<long long>(16, rows / 64));
+  std::vector<std::thread> th;
+  for (int i = 0; i < nt; ++i) th.emplace_back(work, rows * i / nt, rows * (i + 1) / nt);
+  for (auto& x : th) x.join();
+}
+
+// upload one linear map in 8-bit blocks (rows interleaved by mult/add as its
+// dest says) and refresh its dequantised fp16 copy for the matrix-core pass
+static void upload_q8(moshi_ctx* c, const Dest& ds, const moshi_tensor& t) {
+  const Plan& p = c->plan;
+  const long long rows = ds.rows, cols = ds.cols, nb = cols / 32;
+  std::vector<float> host;
+  const float* src = t.data;
+  if (t.on_device) {
+    host.resize((size_t)rows * cols);
+    HIPCHECK(hipMemcpy(host.data(), t.data, host.size() * 4, hipMemcpyDeviceToHost));
+    src = host.data();
+  }
+  std::vector<uint8_t> q((size_t)rows * cols);
+  std::vector<uint32_t> prm((size_t)rows * nb);
+  quantize_rows_q8(src, rows, (int)cols, q.data(), prm.data());
+  // destination rows r * mult + add of the bf16 layout at ds.off
+  char* qd = c->ws + p.q8w + ds.off / 2 + (size_t)ds.add * cols;
+  char* pd = c->ws + p.q8p + ds.off / 16 + (size_t)ds.add * nb * 4;
+  HIPCHECK(hipMemcpy2DAsync(qd, (size_t)ds.mult * cols, q.data(), cols, cols, rows, hipMemcpyHostToDevice, c->stream));
+  HIPCHECK(hipMemcpy2DAsync(pd, (size_t)ds.mult * nb * 4, prm.data(), nb * 4, nb * 4, rows, hipMemcpyHostToDevice,
+                            c->stream));
+  if (p.tf_mfma)
+    launch_q8_to_f16(c->at<uint8_t>(p.q8w + ds.off / 2), c->at<uint32_t>(p.q8p + ds.off / 16),
+                     c->at<uint16_t>(p.w16 + ds.off), rows * ds.mult * cols, c->stream);
+  HIPCHECK(hipGetLastError());
+  HIPCHECK(hipStreamSynchronize(c->stream));  // the host buffers go out of scope
+}
+
 int moshi_init_weights(moshi_ctx* c, const moshi_tensor* t, int n) {
   if (!c) return MOSHI_EINVAL;
   return guard_impl(c, [&] {
@@ -1010,7 +1130,9 @@ int moshi_init_weights(moshi_ctx* c, const moshi_tensor* t, int n) {
              ds.rows * ds.cols);
       const bool bf = p.bf && !ds.f32;
       void* dst = c->ws + ds.off;
-      if (t[i].on_device) {
+      if (p.q8 && ds.linear) {
+        upload_q8(c, ds, t[i]);
+      } else if (t[i].on_device) {
         launch_convert(t[i].data, ds.rows, ds.cols, dst, bf, ds.mult, ds.add, c->stream);
         HIPCHECK(hipGetLastError());
       } else {
@@ -1025,7 +1147,7 @@ int moshi_init_weights(moshi_ctx* c, const moshi_tensor* t, int n) {
           HIPCHECK(hipStreamSynchronize(c->stream));
         }
       }
-      if (bf && p.tf_mfma) {
+      if (bf && p.tf_mfma && !(p.q8 && ds.linear)) {
         // the matrix-core pass reads an fp16 copy (same rounding as converting in the GEMM)
         launch_bf16_to_f16((const uint16_t*)dst, c->at<uint16_t>(p.w16 + ds.off), ds.rows * ds.mult * ds.cols,
                            c->stream);
@@ -1218,7 +1340,7 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
     const bool tf = kernel >= MOSHI_KERNEL_TF_GATE_UP;
     if (tf && (!p.tf_mfma || c->tf_B == 0)) fail(MOSHI_ESTATE, "no matrix-core teacher-forced pass to time");
     if (tf && batch != c->tf_B) fail(MOSHI_EINVAL, "batch %d differs from the last teacher-forced pass (%d)", batch, c->tf_B);
-    const double e = p.esz;
+    const double e = p.q8 ? 1.125 : p.esz;  // bytes per linear weight (8-bit codes + block parameters)
     const double d = g.d_t, F = g.ffn_t, B = batch;
     const long long tfM = (long long)c->tf_B * c->tf_S;
     const double S = c->tf_S;
@@ -1316,6 +1438,30 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
     HIPCHECK(hipGetLastError());
     *avg_us = ms * 1000.f / iters;
     *bytes_per_launch = bytes;
+  });
+}
+
+int moshi_read_q8(moshi_ctx* c, const char* name, uint8_t* codes, uint16_t* scale, uint16_t* mn) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    const Plan& p = c->plan;
+    if (!p.q8) fail(MOSHI_EINVAL, "not an 8-bit model");
+    if (!name || !codes || !scale || !mn) fail(MOSHI_EINVAL, "null argument");
+    auto it = c->dests.find(name);
+    if (it == c->dests.end() || !it->second.linear) fail(MOSHI_EINVAL, "'%s' is not a linear tensor", name);
+    const Dest& ds = it->second;
+    if (!ds.loaded) fail(MOSHI_EINVAL, "'%s' is not loaded", name);
+    const long long rows = ds.rows, cols = ds.cols, nb = cols / 32;
+    std::vector<uint32_t> prm((size_t)rows * nb);
+    HIPCHECK(hipStreamSynchronize(c->stream));
+    HIPCHECK(hipMemcpy2D(codes, cols, c->ws + p.q8w + ds.off / 2 + (size_t)ds.add * cols, (size_t)ds.mult * cols,
+                         cols, rows, hipMemcpyDeviceToHost));
+    HIPCHECK(hipMemcpy2D(prm.data(), nb * 4, c->ws + p.q8p + ds.off / 16 + (size_t)ds.add * nb * 4,
+                         (size_t)ds.mult * nb * 4, nb * 4, rows, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < prm.size(); ++i) {
+      scale[i] = (uint16_t)(prm[i] & 0xffffu);
+      mn[i] = (uint16_t)(prm[i] >> 16);
+    }
   });
 }
 

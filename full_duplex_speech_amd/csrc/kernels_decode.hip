@@ -748,6 +748,365 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, i
 }
 
 // ---------------------------------------------------------------------------
+// Weight-streaming GEMV over 8-bit block weights, one input vector (the
+// 8-bit format of the walkthrough's "压缩Moshi及其对语音质量的影响" section:
+// asymmetric MinMax over blocks of 32 weights of a row, scale and min in
+// float16, w = q * scale + min). Each lane loads 16 codes (half a block) and
+// that block's parameters, and adds scale * sum(q x) + min * sum(x) for its
+// 16 inputs. Blocks hold RG = 8/SK row pairs with SK waves each; wave s of a
+// pair takes the 1024-wide K spans s, s+SK, ... (at most SPW). The prologue
+// and epilogues are the streaming kernels' (one read of x, RMSNorm factor on
+// the dot products, pair_store).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  const uint16_t h = (uint16_t)(v & 0xffffu);
+  return (float)*(const _Float16*)&h;
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  const uint16_t h = (uint16_t)(v >> 16);
+  return (float)*(const _Float16*)&h;
+}
+
+template <int EPI, int SPW>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_q8(GemvArgs a, int SK) {
+  constexpr int EPL = 16, SPAN = 64 * EPL;
+  extern __shared__ float4 xs4[];  // [SK * SPW * SPAN], zero past K
+  __shared__ float s_part[kStreamWaves][2];
+  __shared__ float s_red[kStreamWaves];
+  __shared__ float s_rstd;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+  const int KPAD = SK * SPW * SPAN;
+  const int RG = kStreamWaves / SK;
+  const int npairs = (N + 1) / 2;
+  const int pair = blockIdx.x * RG + wave / SK, sw = wave % SK;
+  const int pr = min(pair, npairs - 1);
+  const int r0 = min(pr * 2, N - 1), r1 = min(pr * 2 + 1, N - 1);
+  const uint8_t* Wq = (const uint8_t*)a.W;
+
+  u32x4 w0[SPW], w1[SPW];
+  uint32_t q0[SPW], q1[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int k = min((sw + i * SK) * SPAN + lane * EPL, K - EPL);
+    w0[i] = __builtin_nontemporal_load((const u32x4*)(Wq + (long long)r0 * K + k));
+    w1[i] = __builtin_nontemporal_load((const u32x4*)(Wq + (long long)r1 * K + k));
+    q0[i] = a.Wq8p[((long long)r0 * K + k) >> 5];
+    q1[i] = a.Wq8p[((long long)r1 * K + k) >> 5];
+  }
+  float p0 = 0.f, p1 = 0.f;
+  int pos = 0, page = 0;
+  if constexpr (EPI == EPI_RESID) {
+    p0 = a.y[r0];
+    p1 = a.y[r1];
+  }
+  if constexpr (EPI == EPI_EMB) {
+    const int t = min(max(a.tok[a.tok_col], 0), a.tok_rows - 1);
+    p0 = bf2f(((const uint16_t*)a.emb)[(long long)t * N + r0]);
+    p1 = bf2f(((const uint16_t*)a.emb)[(long long)t * N + r1]);
+  }
+  if constexpr (EPI == EPI_QKV) {
+    pos = a.pos ? a.pos[0] : a.pos_const;
+    page = a.kv.page_table ? a.kv.page_table[pos / a.kv.pf] : 0;
+    const int dim = (r0 % a.d) % a.hd;
+    const float* cs = a.rope + ((long long)pos * (a.hd >> 1) + (dim >> 1)) * 2;
+    p0 = cs[0];
+    p1 = cs[1];
+  }
+
+  float rs = 0.f;
+  for (int k = tid * 4; k < KPAD; k += 64 * kStreamWaves * 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < K) {
+      v = *(const float4*)(a.x + k);
+      if (a.gain) {
+        rs += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        const float4 g = *(const float4*)(a.gain + k);
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+      }
+    }
+    xs4[k >> 2] = v;
+  }
+  if (a.gain) {
+    rs = wave_sum(rs);
+    if (lane == 0) s_red[wave] = rs;
+  }
+  __syncthreads();
+  if (a.gain && tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) t += s_red[w];
+    s_rstd = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
+  __syncthreads();
+  const float rstd = a.gain ? s_rstd : 1.f;
+
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < SPW; ++i) {
+    const int k = (sw + i * SK) * SPAN + lane * EPL;
+    float xv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const float4 t = xs4[(k + e) >> 2];
+      xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+    }
+    float sx = 0.f, d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const uint32_t c0 = (w0[i][e >> 2] >> (8 * (e & 3))) & 0xffu;
+      const uint32_t c1 = (w1[i][e >> 2] >> (8 * (e & 3))) & 0xffu;
+      sx += xv[e];
+      d0 = fmaf((float)c0, xv[e], d0);
+      d1 = fmaf((float)c1, xv[e], d1);
+    }
+    acc0 = fmaf(f16_lo(q0[i]), d0, fmaf(f16_hi(q0[i]), sx, acc0));
+    acc1 = fmaf(f16_lo(q1[i]), d1, fmaf(f16_hi(q1[i]), sx, acc1));
+  }
+  acc0 = wave_sum(acc0);
+  acc1 = wave_sum(acc1);
+  if (lane == 0) {
+    s_part[wave][0] = acc0;
+    s_part[wave][1] = acc1;
+  }
+  __syncthreads();
+  if (sw != 0 || lane != 0 || pair >= npairs) return;
+  float t0 = 0.f, t1 = 0.f;
+  for (int w = 0; w < SK; ++w) {
+    t0 += s_part[wave + w][0];
+    t1 += s_part[wave + w][1];
+  }
+  pair_store<EPI>(a, a.y, pair * 2, t0 * rstd, t1 * rstd, p0, p1, pos, page);
+}
+
+// Persistent 8-bit variant for matrices with at least as many row pairs as the
+// chip runs waves (the temporal maps, the text head): the streaming kernels'
+// persistent schedule (units of one row pair and LPG 1024-wide spans, dealt
+// round-robin to about two blocks per CU, each unit's registers refilled with
+// the next unit's codes and block parameters right after use) with the 8-bit
+// lane layout above.
+template <int EPI, int LPG>
+__global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_q8_persist(GemvArgs a) {
+  constexpr int EPL = 16, SPAN = 64 * EPL, GROUP = SPAN * LPG;
+  extern __shared__ float4 xs4[];  // [KP], zero past K
+  __shared__ float s_red[kStreamWaves];
+  __shared__ float s_rstd;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.K, N = a.N;
+  const int ng = (K + GROUP - 1) / GROUP;
+  const int KP = ng * GROUP;
+  const int npairs = (N + 1) / 2;
+  const int nw = gridDim.x * kStreamWaves;
+  const int gw = blockIdx.x * kStreamWaves + wave;
+  const int mine = gw < npairs ? (npairs - 1 - gw) / nw + 1 : 0;
+  const int units = mine * ng;
+  const uint8_t* Wq = (const uint8_t*)a.W;
+
+  int pos = 0, page = 0, tok = 0;
+  if constexpr (EPI == EPI_QKV) {
+    pos = a.pos ? a.pos[0] : a.pos_const;
+    page = a.kv.page_table ? a.kv.page_table[pos / a.kv.pf] : 0;
+  }
+  if constexpr (EPI == EPI_EMB) tok = min(max(a.tok[a.tok_col], 0), a.tok_rows - 1);
+
+  u32x4 w0[LPG], w1[LPG];
+  uint32_t q0[LPG], q1[LPG];
+  auto load_slot = [&](int pair, int g, int i) {
+    const int k = min(g * GROUP + i * SPAN + lane * EPL, K - EPL);
+    const long long o0 = (long long)min(pair * 2, N - 1) * K + k;
+    const long long o1 = (long long)min(pair * 2 + 1, N - 1) * K + k;
+    w0[i] = __builtin_nontemporal_load((const u32x4*)(Wq + o0));
+    w1[i] = __builtin_nontemporal_load((const u32x4*)(Wq + o1));
+    q0[i] = __builtin_nontemporal_load(a.Wq8p + (o0 >> 5));
+    q1[i] = __builtin_nontemporal_load(a.Wq8p + (o1 >> 5));
+  };
+  if (units > 0) {
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) load_slot(gw, 0, i);
+  }
+
+  float rs = 0.f;
+  for (int k = tid * 4; k < KP; k += 64 * kStreamWaves * 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (k < K) {
+      v = *(const float4*)(a.x + k);
+      if (a.gain) {
+        rs += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        const float4 g = *(const float4*)(a.gain + k);
+        v.x *= g.x; v.y *= g.y; v.z *= g.z; v.w *= g.w;
+      }
+    }
+    xs4[k >> 2] = v;
+  }
+  if (a.gain) {
+    rs = wave_sum(rs);
+    if (lane == 0) s_red[wave] = rs;
+  }
+  __syncthreads();
+  if (a.gain && tid == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kStreamWaves; ++w) t += s_red[w];
+    s_rstd = 1.0f / sqrtf(t / (float)K + a.eps);
+  }
+  __syncthreads();
+  if (units == 0) return;
+  const float rstd = a.gain ? s_rstd : 1.f;
+
+  // epilogue operands, loaded one row pair ahead
+  auto load_pre = [&](int pair, float& e0, float& e1) {
+    const int r0 = min(pair * 2, N - 1), r1 = min(pair * 2 + 1, N - 1);
+    e0 = 0.f;
+    e1 = 0.f;
+    if constexpr (EPI == EPI_RESID) {
+      e0 = a.y[r0];
+      e1 = a.y[r1];
+    }
+    if constexpr (EPI == EPI_EMB) {
+      e0 = bf2f(((const uint16_t*)a.emb)[(long long)tok * N + r0]);
+      e1 = bf2f(((const uint16_t*)a.emb)[(long long)tok * N + r1]);
+    }
+    if constexpr (EPI == EPI_QKV) {
+      const int dim = (r0 % a.d) % a.hd;
+      const float* cs = a.rope + ((long long)pos * (a.hd >> 1) + (dim >> 1)) * 2;
+      e0 = cs[0];
+      e1 = cs[1];
+    }
+  };
+  float pre0, pre1, nxt0 = 0.f, nxt1 = 0.f;
+  load_pre(gw, pre0, pre1);
+  float acc0 = 0.f, acc1 = 0.f;
+
+  auto unit = [&](int pair, int g, int npair, int ngrp, bool refill) {
+    if (refill) load_pre(npair, nxt0, nxt1);
+#pragma unroll
+    for (int i = 0; i < LPG; ++i) {
+      const int k = g * GROUP + i * SPAN + lane * EPL;
+      float xv[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        const float4 t = xs4[(k + e) >> 2];
+        xv[e] = t.x; xv[e + 1] = t.y; xv[e + 2] = t.z; xv[e + 3] = t.w;
+      }
+      float sx = 0.f, d0 = 0.f, d1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        sx += xv[e];
+        d0 = fmaf((float)((w0[i][e >> 2] >> (8 * (e & 3))) & 0xffu), xv[e], d0);
+        d1 = fmaf((float)((w1[i][e >> 2] >> (8 * (e & 3))) & 0xffu), xv[e], d1);
+      }
+      acc0 = fmaf(f16_lo(q0[i]), d0, fmaf(f16_hi(q0[i]), sx, acc0));
+      acc1 = fmaf(f16_lo(q1[i]), d1, fmaf(f16_hi(q1[i]), sx, acc1));
+      if (refill) load_slot(npair, ngrp, i);
+    }
+    if (g == ng - 1) {
+      acc0 = wave_sum(acc0);
+      acc1 = wave_sum(acc1);
+      if (lane == 0) pair_store<EPI>(a, a.y, pair * 2, acc0 * rstd, acc1 * rstd, pre0, pre1, pos, page);
+      acc0 = 0.f;
+      acc1 = 0.f;
+    }
+    if (refill && ngrp == 0) {
+      pre0 = nxt0;
+      pre1 = nxt1;
+    }
+  };
+
+  int pair = gw, g = 0;
+  for (int u = 0; u < units - 1; ++u) {
+    int npair = pair, ngrp = g + 1;
+    if (ngrp == ng) {
+      ngrp = 0;
+      npair += nw;
+    }
+    unit(pair, g, npair, ngrp, true);
+    pair = npair;
+    g = ngrp;
+  }
+  unit(pair, g, pair, g, false);
+}
+
+template <int LPG>
+static void q8_persist_launch(const GemvArgs& a, int epi, int blocks, hipStream_t s) {
+  constexpr int GROUP = 1024 * LPG;
+  const size_t lds = (size_t)((a.K + GROUP - 1) / GROUP) * GROUP * sizeof(float);
+  const int T = 64 * kStreamWaves;
+  switch (epi) {
+    case EPI_STORE: k_gemv_q8_persist<EPI_STORE, LPG><<<blocks, T, lds, s>>>(a); break;
+    case EPI_RESID: k_gemv_q8_persist<EPI_RESID, LPG><<<blocks, T, lds, s>>>(a); break;
+    case EPI_EMB: k_gemv_q8_persist<EPI_EMB, LPG><<<blocks, T, lds, s>>>(a); break;
+    case EPI_SWIGLU: k_gemv_q8_persist<EPI_SWIGLU, LPG><<<blocks, T, lds, s>>>(a); break;
+    case EPI_QKV: k_gemv_q8_persist<EPI_QKV, LPG><<<blocks, T, lds, s>>>(a); break;
+  }
+}
+
+template <int SPW>
+static void q8_launch(const GemvArgs& a, int epi, int SK, hipStream_t s) {
+  const int RG = kStreamWaves / SK;
+  dim3 grid(((a.N + 1) / 2 + RG - 1) / RG);
+  const size_t lds = (size_t)SK * SPW * 1024 * sizeof(float);
+  const int T = 64 * kStreamWaves;
+  switch (epi) {
+    case EPI_STORE: k_gemv_q8<EPI_STORE, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_RESID: k_gemv_q8<EPI_RESID, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_EMB: k_gemv_q8<EPI_EMB, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_SWIGLU: k_gemv_q8<EPI_SWIGLU, SPW><<<grid, T, lds, s>>>(a, SK); break;
+    case EPI_QKV: k_gemv_q8<EPI_QKV, SPW><<<grid, T, lds, s>>>(a, SK); break;
+  }
+}
+
+static int device_cus();
+
+static void gemv_q8(const GemvArgs& a, int B, int epi, hipStream_t s) {
+  if (B != 1) throw std::runtime_error("8-bit weights stream one input vector per launch");
+  if (a.K % 32 != 0 || a.K < 16) throw std::runtime_error("8-bit weights need K % 32 == 0");
+  const int npairs = (a.N + 1) / 2;
+  const int nspans = (a.K + 1023) / 1024;
+  constexpr int kWaves = 2048;
+  if (npairs >= kWaves) {
+    // persistent: spans per unit that pad K least (the inputs, padded to whole
+    // units, must fit in 64 KB of LDS)
+    const int lpg = nspans % 8 == 0 ? 8 : (nspans <= 2 ? 2 : 4);
+    const long long kp = (long long)((nspans + lpg - 1) / lpg) * lpg * 1024;
+    if (kp * (long long)sizeof(float) <= 65536) {
+      const int blocks = std::min((npairs + kStreamWaves - 1) / kStreamWaves, 2 * device_cus());
+      if (lpg == 2) q8_persist_launch<2>(a, epi, blocks, s);
+      else if (lpg == 4) q8_persist_launch<4>(a, epi, blocks, s);
+      else q8_persist_launch<8>(a, epi, blocks, s);
+      return;
+    }
+  }
+  // split K inside a block while the grid has fewer than 2048 waves or a wave
+  // would need more than 8 spans
+  int SK = 1;
+  while (SK < kStreamWaves && SK * 2 <= nspans && (npairs * SK < kWaves || (nspans + SK - 1) / SK > 8)) SK *= 2;
+  const int need = (nspans + SK - 1) / SK;
+  if (need > 8) throw std::runtime_error("8-bit GEMV: rows too long");
+  const int spw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
+  if ((size_t)SK * spw * 1024 * sizeof(float) > 65536) throw std::runtime_error("8-bit GEMV: inputs exceed LDS");
+  if (spw == 1) q8_launch<1>(a, epi, SK, s);
+  else if (spw == 2) q8_launch<2>(a, epi, SK, s);
+  else if (spw == 4) q8_launch<4>(a, epi, SK, s);
+  else q8_launch<8>(a, epi, SK, s);
+}
+
+__global__ __launch_bounds__(256) void k_q8_to_f16(const uint8_t* q, const uint32_t* prm, uint16_t* dst, long long n) {
+  for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const uint32_t pv = prm[i >> 5];
+    const float v = fmaf((float)q[i], f16_lo(pv), f16_hi(pv));
+    const _Float16 h = (_Float16)v;
+    dst[i] = *(const uint16_t*)&h;
+  }
+}
+
+void launch_q8_to_f16(const uint8_t* q, const uint32_t* params, uint16_t* dst, long long n, hipStream_t s) {
+  long long blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  k_q8_to_f16<<<(unsigned)blocks, 256, 0, s>>>(q, params, dst, n);
+}
+
+// ---------------------------------------------------------------------------
 // Batched weight-streaming GEMV on matrix cores (2..16 conversations, bf16
 // weights). v_mfma_f32_16x16x32_f16 computes a 16 (rows of W) x 16 (tokens)
 // tile: lane l supplies W[row0 + l%16][k0 + 8*(l/16) .. +7] (a 16-byte load)
@@ -1199,6 +1558,11 @@ static void no_stats(const GemvArgs& a) {
 }
 
 void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s) {
+  if (a.Wq8p) {
+    if (a.stat_in || a.stat_out) throw std::runtime_error("8-bit GEMV takes no statistics hand-off");
+    gemv_q8(a, B, epi, s);
+    return;
+  }
   // batched bf16: matrix cores, when the fp16 inputs fit in LDS
   if (bf16 && B >= 2 && B <= 16 && (size_t)B * ((a.K + 255) / 256 * 256) * 2 <= 65536 * 3 && a.K % 8 == 0 &&
       a.N % 4 == 0) {

@@ -48,6 +48,9 @@ struct GemvArgs {
   KvView kv;
   int kv_bf16;
   int layer;
+  // 8-bit block weights (when set): W holds the codes q [N][K] (uint8) and
+  // Wq8p the blocks' (scale | min << 16) float16 pairs [N][K/32]; w = q * scale + min
+  const uint32_t* Wq8p;
   // EPI_SWIGLU: when set, also an fp16 copy of the outputs, [B][ldy]
   uint16_t* y16;
   // batched matrix-core path, RMSNorm statistics without re-reading x:
@@ -196,6 +199,8 @@ void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, h
 void launch_embed(const EmbedArgs& a, int B, bool bf16, hipStream_t s);
 void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s);
 void launch_advance(const AdvanceArgs& a, int B, hipStream_t s);
+// 8-bit blocks -> fp16 (w = q * scale + min), n elements from the start of a block
+void launch_q8_to_f16(const uint8_t* q, const uint32_t* params, uint16_t* dst, long long n, hipStream_t s);
 // bf16 -> fp16 element copy (round to nearest even; |x| > 65504 -> inf)
 void launch_bf16_to_f16(const uint16_t* src, uint16_t* dst, long long n, hipStream_t s);
 void launch_convert(const float* src, long long rows, int cols, void* dst, bool bf16, long long dst_row_mult,

@@ -49,6 +49,9 @@ extern "C" {
 /* weight precision (moshi_config.dtype) */
 #define MOSHI_F32 0
 #define MOSHI_BF16 1
+#define MOSHI_Q8 2 /* linear maps in 8-bit blocks of 32 (asymmetric MinMax, float16 scale and min;
+                      walkthrough section "压缩Moshi及其对语音质量的影响", "量化格式"), quantised at
+                      upload from the bf16-rounded weights; embeddings bf16, norms fp32; max_batch 1 */
 
 /* flags */
 #define MOSHI_DEVICE_PTRS 1   /* all array arguments are device pointers; the call
@@ -69,7 +72,7 @@ typedef struct moshi_config {
   int32_t n_q;                               /* codebooks per speaker; must be 8 */
   int32_t delay;                             /* acoustic delay tau, in frames (>= 0) */
   float rope_base, norm_eps;                 /* RoPE base, RMSNorm epsilon */
-  int32_t dtype;                             /* MOSHI_F32 or MOSHI_BF16 weights */
+  int32_t dtype;                             /* MOSHI_F32, MOSHI_BF16 or MOSHI_Q8 weights */
   int32_t max_batch;                         /* conversations per context (1..8) */
   int32_t page_frames;                       /* KV page size in frames (64) */
   int32_t n_pages;                           /* KV pages in the pool; 0 = max_batch*ceil(ctx_max/page_frames) */
@@ -182,6 +185,14 @@ int moshi_forward_teacher_forced(moshi_ctx* ctx, const int32_t* tokens, int32_t 
  * The conversation state is left unchanged except for scratch activations. */
 int moshi_time_kernel(moshi_ctx* ctx, int32_t kernel, int32_t batch, int32_t iters, float* avg_us,
                       double* bytes_per_launch);
+
+/* MOSHI_Q8 models: copy the stored 8-bit form of linear tensor `name` (as named
+ * for moshi_init_weights, [rows][cols]) to host buffers: codes[rows][cols],
+ * and per block of 32 weights of a row scale[rows][cols/32] and
+ * min[rows][cols/32] (float16 bit patterns); a weight is codes * scale + min.
+ * MOSHI_EINVAL for an unknown, non-linear or not-yet-loaded tensor or a model
+ * that is not MOSHI_Q8. */
+int moshi_read_q8(moshi_ctx* ctx, const char* name, uint8_t* codes, uint16_t* scale, uint16_t* min);
 
 /* Wait for queued work; reports device-side id errors of MOSHI_DEVICE_PTRS calls. */
 int moshi_sync(moshi_ctx* ctx);

@@ -88,3 +88,17 @@ def test_create_rejects_bad_arguments_without_touching_the_device(fds):
     with pytest.raises(fds.MoshiError) as e:
         fds.moshi_create(c, 0, 1 << 20, 16)  # too small: rejected before any device access
     assert e.value.code == fds.binding.MOSHI_ENOMEM
+
+
+def test_q8_config_rules(fds):
+    """8-bit models stream one conversation and need 32-aligned linear inputs; their
+    workspace adds the codes (half the bf16 weight bytes) and the block parameters."""
+    cfg = config("mid_q8")
+    ok = fds.config_struct(cfg, max_batch=1)
+    bad = fds.config_struct(cfg, max_batch=2)
+    assert fds.moshi_check_config(ok)[0] == 0
+    rc, msg = fds.moshi_check_config(bad)
+    assert rc != 0 and "max_batch" in msg
+    bf = fds.config_struct(config("mid_bf16"), max_batch=1)
+    extra = fds.moshi_workspace_bytes(ok) - fds.moshi_workspace_bytes(bf)
+    assert extra > 0
