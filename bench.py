@@ -59,20 +59,34 @@ def log(msg):
 
 
 def joint_prompt(fds, cfg, b, n_frames, seed=0):
-    """Random codec frames -> model-order frames [n, 17] (delay applied by the library's helper)."""
+    """Random codec frames -> model-order frames [n, 17] (acoustic delay applied by the
+    library's helper; a text-audio delay shifts the later modality, pad first)."""
     from synth import raw_frames
     fr = raw_frames(cfg, b, n_frames, seed)
     V = np.empty((n_frames, 17), np.int32)
     V[:, 0] = fr["text"]
     V[:, 1:9] = fds.moshi_delay_codes(fr["moshi"], cfg.delay, cfg.pad_audio)
     V[:, 9:] = fds.moshi_delay_codes(fr["user"], cfg.delay, cfg.pad_audio)
+    t0, a0 = max(cfg.text_delay, 0), max(-cfg.text_delay, 0)
+    if t0:
+        V[t0:, 0] = V[:-t0, 0].copy()
+        V[:t0, 0] = cfg.pad_text
+    if a0:
+        V[a0:, 1:] = V[:-a0, 1:].copy()
+        V[:a0, 1:] = cfg.pad_audio
     return V
+
+
+def tts_words(cfg, b, n_words=4096):
+    """Random words of 1-3 text ids (ids 0 and 1 stand for PAD and EPAD)."""
+    rng = np.random.default_rng([11, b])
+    return [list(rng.integers(2, cfg.vocab_text, size=int(rng.integers(1, 4)))) for _ in range(n_words)]
 
 
 def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
     """The oracle (float32) on the host: prefill untimed, then `frames` greedy frames
-    of conversation 0 timed."""
-    from oracle import Oracle, Session, dequantized_weights
+    of conversation 0 timed, in the configuration's streaming mode."""
+    from oracle import Oracle, Session, TtsTextControl, dequantized_weights
     cores = len(os.sched_getaffinity(0))
     if cfg.dtype == "q8":  # the 8-bit model computes with the quantise-dequantise image of its linear maps
         weights = dequantized_weights(weights)
@@ -84,9 +98,14 @@ def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
         sess.pos = P
         sess.prev = prompts[0][P - 1].copy()
     t_prefill = time.perf_counter() - t0
+    ctl = TtsTextControl(tts_words(cfg, 0), 0, 1, 0.65, 0.5) if cfg.mode == "tts" else None
     t0 = time.perf_counter()
     for i in range(frames):
-        sess.step(users[0][P + i])
+        if cfg.mode == "asr":
+            force = np.concatenate([[-1], prompts[0][P + i, 1:9]])
+            sess.step(users[0][P + i], force=force, text_only=True)
+        else:
+            sess.step(users[0][P + i], text_choice=ctl.choose if ctl else None)
     dt = time.perf_counter() - t0
     return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
             "sample": f"{frames} greedy frames of one conversation at positions {P}..{P + frames - 1} "
@@ -131,7 +150,7 @@ def main():
     weights = generate_weights(cfg, seed=0)
     log(f"weights: {param_count(cfg) / 1e9:.3f} B params generated in {time.perf_counter() - t0:.1f} s")
     max_tf = B * cfg.tf_frames if tf_mode else 0
-    eng = fds.Moshi(cfg, max_batch=B, max_tf_tokens=max_tf)
+    eng = fds.Moshi(cfg, max_batch=B, max_tf_tokens=max_tf, tts_max_tokens=16384 if cfg.mode == "tts" else 0)
     t0 = time.perf_counter()
     eng.load_weights(weights)
     log(f"weights uploaded in {time.perf_counter() - t0:.1f} s; workspace {eng.ws_bytes / 1e9:.2f} GB")
@@ -161,6 +180,15 @@ def main():
         users = [p[:, 9:] for p in prompts]
         user_dev = torch.from_numpy(np.stack([users[b][P:P + max(K, W)] for b in range(B)], axis=1).copy()).cuda()
         out_dev = torch.empty((max(K, W), B, 9), dtype=torch.int32, device="cuda")
+        flags = fds.MOSHI_DEVICE_PTRS
+        force_dev = [None] * max(K, W)
+        if cfg.mode == "asr":
+            # streaming ASR: Moshi's audio is forced from the input, the text is free, no depth
+            f = np.stack([prompts[b][P:P + max(K, W)] for b in range(B)], axis=1)[..., :9].copy()
+            f[..., 0] = -1
+            force_all = torch.from_numpy(f).cuda()
+            force_dev = [force_all[i] for i in range(max(K, W))]
+            flags |= fds.MOSHI_STEP_TEXT_ONLY
         torch.cuda.synchronize()
 
         def prefill():
@@ -168,25 +196,31 @@ def main():
             if P:
                 pr = np.ascontiguousarray(np.stack([p[:P] for p in prompts]))
                 fds.moshi_forward_teacher_forced(ctx, pr, B, P, fds.MOSHI_TF_FILL_KV | fds.MOSHI_TF_SKIP_DEPTH)
+            if cfg.mode == "tts":
+                for b in range(B):
+                    fds.moshi_tts_text(ctx, b, tts_words(cfg, b), 0, 1, 0.65, 0.5)
 
         t0 = time.perf_counter()
         prefill()
         log(f"prefill {B} x {P} frames in {time.perf_counter() - t0:.2f} s")
         for i in range(W):
-            fds.moshi_step(ctx, B, user_dev[i], None, out_dev[i], None, None, fds.MOSHI_DEVICE_PTRS)
+            fds.moshi_step(ctx, B, user_dev[i], force_dev[i], out_dev[i], None, None, flags)
         fds.moshi_sync(ctx)
         prefill()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            fds.moshi_step(ctx, B, user_dev[i], None, out_dev[i], None, None, fds.MOSHI_DEVICE_PTRS)
+            fds.moshi_step(ctx, B, user_dev[i], force_dev[i], out_dev[i], None, None, flags)
         fds.moshi_sync(ctx)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         frames_per_step = B
         log(f"{K} steps of {B} frame(s): {dt * 1000 / K:.3f} ms/step; last tokens {out_dev[K - 1, 0].tolist()}")
         shape = "7B-shape, 8-bit block weights" if cfg.dtype == "q8" else "7B-shape"
-        workload = {"workload": f"{shape} streaming decode, batch {B}, {P}-frame prompt then {K} greedy frames"
+        what = {"asr": "streaming ASR (text 2 s behind the audio, audio forced, depth skipped)",
+                "tts": "streaming TTS (audio 2 s behind the text, in-kernel text control)"}.get(cfg.mode,
+                                                                                              "streaming decode")
+        workload = {"workload": f"{shape} {what}, batch {B}, {P}-frame prompt then {K} greedy frames"
                     if cfg.d_t == 4096 else f"{cfg.name} streaming decode, batch {B}, {P}-frame prompt then "
                     f"{K} greedy frames", "config": cfg.name, "batch": B, "prompt_frames": P, "frames": K}
 
@@ -213,7 +247,8 @@ def main():
     else:
         us, nbytes = fds.moshi_time_kernel(ctx, "ffn_gate_up", B, args.kernel_iters)
         ach = nbytes / (us * 1e-6) / 1e9
-        traffic = measured_traffic() if (cfg.name == "b1_7b" and B == 1) else None
+        # the counters were taken on this kernel at this shape (7B, bf16, one conversation)
+        traffic = measured_traffic() if (cfg.d_t == 4096 and cfg.dtype == "bf16" and B == 1) else None
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": ("k_gemv_q8" if cfg.dtype == "q8" else "k_gemv") +
@@ -230,6 +265,9 @@ def main():
         lin_esz = 1.125 if cfg.dtype == "q8" else esz
         lin = param_count(cfg) - (cfg.vocab_text + 1 + 16 * (cfg.codebook + 1)) * cfg.d_t \
             - (cfg.vocab_text + 1 + 7 * (cfg.codebook + 1)) * cfg.d_d
+        if cfg.mode == "asr":  # no depth: the temporal layers, the norms and the text head only
+            lin = cfg.n_layers_t * (4 * cfg.d_t ** 2 + 3 * cfg.d_t * cfg.ffn_t + 2 * cfg.d_t) \
+                + cfg.vocab_text * cfg.d_t + cfg.d_t
         mean_ctx = P + (K + 1) / 2
         kv = B * cfg.n_layers_t * 2 * cfg.d_t * esz * mean_ctx
         frame_bytes = lin * lin_esz + kv

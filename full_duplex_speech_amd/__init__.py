@@ -6,6 +6,7 @@ include/moshi.h); this package holds its ctypes binding and build script.
 from .binding import (  # noqa: F401
     MOSHI_BF16,
     MOSHI_Q8,
+    MOSHI_STEP_TEXT_ONLY,
     MOSHI_DEVICE_PTRS,
     MOSHI_F32,
     MOSHI_TF_FILL_KV,
@@ -24,6 +25,7 @@ from .binding import (  # noqa: F401
     moshi_loss,
     moshi_position,
     moshi_read_q8,
+    moshi_tts_text,
     moshi_reset,
     moshi_step,
     moshi_sync,

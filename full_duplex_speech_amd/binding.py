@@ -26,6 +26,7 @@ MOSHI_Q8 = 2
 MOSHI_DEVICE_PTRS = 1
 MOSHI_TF_FILL_KV = 2
 MOSHI_TF_SKIP_DEPTH = 4
+MOSHI_STEP_TEXT_ONLY = 8
 
 _ERR_NAMES = {-1: "EINVAL", -2: "ECONTEXT", -3: "ENOMEM", -4: "EHIP", -5: "ESTATE"}
 
@@ -41,7 +42,8 @@ class moshi_config(ctypes.Structure):
                                                "d_d", "n_layers_d", "n_heads_d", "ffn_d",
                                                "vocab_text", "codebook", "n_q", "delay")] + \
                [("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float)] + \
-               [(n, ctypes.c_int32) for n in ("dtype", "max_batch", "page_frames", "n_pages", "max_tf_tokens")]
+               [(n, ctypes.c_int32) for n in ("dtype", "max_batch", "page_frames", "n_pages", "max_tf_tokens",
+                                              "text_delay", "tts_max_tokens")]
 
 
 class moshi_tensor(ctypes.Structure):
@@ -58,6 +60,7 @@ EXPORTS = (
     "moshi_workspace_bytes", "moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset",
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
     "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel", "moshi_read_q8",
+    "moshi_tts_text",
 )
 KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5, "tf_gate_up": 6,
            "tf_attn": 7}
@@ -90,11 +93,12 @@ def lib() -> ctypes.CDLL:
     L.moshi_last_error.restype = ctypes.c_char_p
     L.moshi_time_kernel.argtypes = [VP, I32, I32, I32, P(ctypes.c_float), P(ctypes.c_double)]
     L.moshi_read_q8.argtypes = [VP, ctypes.c_char_p, VP, VP, VP]
+    L.moshi_tts_text.argtypes = [VP, I32, VP, VP, I32, I32, I32, ctypes.c_float, ctypes.c_float]
     L.moshi_destroy.argtypes = [VP]
     L.moshi_destroy.restype = None
     for n in ("moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset", "moshi_step",
               "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
-              "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8"):
+              "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8", "moshi_tts_text"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -122,7 +126,7 @@ def _check(ctx, rc: int):
 
 
 def config_struct(cfg, max_batch: Optional[int] = None, page_frames: int = 64, n_pages: int = 0,
-                  max_tf_tokens: int = 0) -> moshi_config:
+                  max_tf_tokens: int = 0, tts_max_tokens: int = 0) -> moshi_config:
     """Fill the C config from any object with the model's shape attributes."""
     c = moshi_config()
     for n in ("d_t", "n_layers_t", "n_heads_t", "ffn_t", "ctx_max", "d_d", "n_layers_d", "n_heads_d", "ffn_d",
@@ -135,6 +139,8 @@ def config_struct(cfg, max_batch: Optional[int] = None, page_frames: int = 64, n
     c.page_frames = page_frames
     c.n_pages = n_pages
     c.max_tf_tokens = max_tf_tokens
+    c.text_delay = int(getattr(cfg, "text_delay", 0))
+    c.tts_max_tokens = tts_max_tokens
     return c
 
 
@@ -232,6 +238,16 @@ def moshi_read_q8(ctx, name: str, rows: int, cols: int):
     return codes, scale.view(np.float16), mn.view(np.float16)
 
 
+def moshi_tts_text(ctx, conv: int, words, pad_id: int, epad_id: int, target_pad_ratio: float, bonus: float) -> None:
+    """Zero-shot TTS text control of conversation ``conv``: ``words`` is a list of
+    token-id lists in speaking order (an empty list switches the control off)."""
+    toks = np.ascontiguousarray([t for w in words for t in w], dtype=np.int32)
+    lens = np.ascontiguousarray([len(w) for w in words], dtype=np.int32)
+    _check(ctx, lib().moshi_tts_text(ctx, conv, toks.ctypes.data if toks.size else None,
+                                     lens.ctypes.data if lens.size else None, int(lens.size), pad_id, epad_id,
+                                     target_pad_ratio, bonus))
+
+
 def moshi_last_error(ctx) -> str:
     return lib().moshi_last_error(ctx).decode()
 
@@ -246,14 +262,14 @@ class Moshi:
     """One context with a torch-allocated workspace on the current GPU."""
 
     def __init__(self, cfg, max_batch: Optional[int] = None, page_frames: int = 64, n_pages: int = 0,
-                 max_tf_tokens: int = 0, device: Optional[int] = None):
+                 max_tf_tokens: int = 0, device: Optional[int] = None, tts_max_tokens: int = 0):
         import torch
         if not torch.cuda.is_available():
             raise RuntimeError("the HIP library needs a GPU; none is visible")
         if device is not None:
             torch.cuda.set_device(device)
         self.cfg = cfg
-        self.c = config_struct(cfg, max_batch, page_frames, n_pages, max_tf_tokens)
+        self.c = config_struct(cfg, max_batch, page_frames, n_pages, max_tf_tokens, tts_max_tokens)
         rc, msg = moshi_check_config(self.c)
         if rc:
             raise MoshiError(rc, msg)
@@ -284,17 +300,22 @@ class Moshi:
     def position(self, b: int = 0) -> int:
         return moshi_position(self.ctx, b)
 
-    def step(self, user_codes: np.ndarray, force: Optional[np.ndarray] = None, logits: bool = False):
-        """Host-pointer step: returns (tokens [B, 9], text_logits, audio_logits)."""
+    def step(self, user_codes: np.ndarray, force: Optional[np.ndarray] = None, logits: bool = False,
+             text_only: bool = False):
+        """Host-pointer step: returns (tokens [B, 9], text_logits, audio_logits).
+        ``force`` entries of -1 leave a slot to the model; ``text_only`` skips the depth."""
         cfg = self.cfg
         u = np.ascontiguousarray(user_codes, dtype=np.int32).reshape(-1, 8)
         B = u.shape[0]
         f = None if force is None else np.ascontiguousarray(force, dtype=np.int32).reshape(B, 9)
         tok = np.empty((B, 9), dtype=np.int32)
         lt = np.empty((B, cfg.vocab_text), dtype=np.float32) if logits else None
-        la = np.empty((B, cfg.n_q, cfg.codebook), dtype=np.float32) if logits else None
-        moshi_step(self.ctx, B, u, f, tok, lt, la, 0)
+        la = np.empty((B, cfg.n_q, cfg.codebook), dtype=np.float32) if logits and not text_only else None
+        moshi_step(self.ctx, B, u, f, tok, lt, la, MOSHI_STEP_TEXT_ONLY if text_only else 0)
         return tok, lt, la
+
+    def tts_text(self, words, pad_id: int, epad_id: int, target_pad_ratio: float, bonus: float, conv: int = 0):
+        moshi_tts_text(self.ctx, conv, words, pad_id, epad_id, target_pad_ratio, bonus)
 
     def forward_teacher_forced(self, tokens: np.ndarray, fill_kv: bool = False, skip_depth: bool = False,
                                logits: bool = True, loss: bool = True):

@@ -12,6 +12,7 @@
 #include <functional>
 #include <map>
 #include <string>
+#include <cmath>
 #include <thread>
 #include <utility>
 #include <vector>
@@ -92,6 +93,9 @@ struct Plan {
   // state (int32)
   size_t st_pos = 0, st_prev = 0, st_in = 0, st_out_tok = 0, st_cur_tok = 0, st_err = 0, st_cnt_t = 0,
          st_cnt_d = 0, st_end = 0;
+  // TTS text control: per conversation kTtsCtl words of state (zeroed with the
+  // step state: off), then the text and its word-start flags
+  size_t tts_ctl = 0, tts_tok = 0, tts_start = 0;
   size_t st_user = 0, st_force = 0, st_has_force = 0;
   // activations (float32)
   size_t h = 0, q = 0, attn = 0, inter = 0, inter16 = 0, dinter16 = 0, part_t = 0, text_logits = 0;
@@ -125,6 +129,8 @@ int validate(const moshi_config& c, std::string& msg) {
   if (c.n_q != 8) return bad("n_q must be 8 (K = 17 sub-streams)");
   if (c.vocab_text < 2 || c.codebook < 2) return bad("vocabularies must have at least 2 entries");
   if (c.delay < 0) return bad("delay must be >= 0");
+  if (c.text_delay <= -c.ctx_max || c.text_delay >= c.ctx_max) return bad("|text_delay| must be below ctx_max");
+  if (c.tts_max_tokens < 0 || c.tts_max_tokens > (1 << 24)) return bad("tts_max_tokens must be in 0..2^24");
   if (!(c.rope_base > 0.f) || !(c.norm_eps > 0.f)) return bad("rope_base and norm_eps must be positive");
   if (c.dtype != MOSHI_F32 && c.dtype != MOSHI_BF16 && c.dtype != MOSHI_Q8)
     return bad("dtype must be MOSHI_F32, MOSHI_BF16 or MOSHI_Q8");
@@ -217,7 +223,12 @@ Plan make_plan(const moshi_config& c) {
   p.st_err = p.take(4);
   p.st_cnt_t = p.take(mb * c.n_heads_t * 4);
   p.st_cnt_d = p.take(mb * c.n_heads_d * 4);
+  if (c.tts_max_tokens) p.tts_ctl = p.take(mb * kTtsCtl * 4);
   p.st_end = p.total;
+  if (c.tts_max_tokens) {
+    p.tts_tok = p.take((size_t)mb * c.tts_max_tokens * 4);
+    p.tts_start = p.take((size_t)mb * c.tts_max_tokens * 4);
+  }
   // activations
   p.h = p.take(mb * d * 4);
   p.q = p.take(mb * d * 4);
@@ -530,9 +541,17 @@ ArgmaxArgs argmax_args(moshi_ctx* c, int slot) {
     m.ld = g.n_q * g.codebook;
   }
   m.slot = slot;
-  m.pad_after = slot >= 2;
-  m.pad_id = g.codebook;
-  m.delay = g.delay;
+  // own slots are pad until their stream starts: the text after max(text_delay, 0)
+  // frames, the audio after max(-text_delay, 0), the acoustic codebooks delay later
+  const int text_start = std::max(g.text_delay, 0), audio_start = std::max(-g.text_delay, 0);
+  m.start = slot == 0 ? text_start : (slot == 1 ? audio_start : audio_start + g.delay);
+  m.pad_id = slot == 0 ? g.vocab_text : g.codebook;
+  if (slot == 0 && g.tts_max_tokens) {
+    m.tts_ctl = c->at<int>(p.tts_ctl);
+    m.tts_tok = c->at<int>(p.tts_tok);
+    m.tts_start = c->at<int>(p.tts_start);
+    m.tts_cap = g.tts_max_tokens;
+  }
   m.pos = c->at<int>(p.st_pos);
   m.out_tok = c->at<int>(p.st_out_tok);
   m.cur_tok = c->at<int>(p.st_cur_tok);
@@ -668,6 +687,8 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   av.err = c->at<int>(p.st_err);
   av.pad_text = g.vocab_text;
   av.pad_audio = g.codebook;
+  av.text_only = depth ? 0 : 1;
+  av.out_tok = c->at<int>(p.st_out_tok);
   launch_advance(av, B, s);
   HIPCHECK(hipGetLastError());
 }
@@ -905,6 +926,10 @@ void reset_conv(moshi_ctx* c, int b) {
   for (int ph : c->pages[b]) c->free_pages.push_back(ph);
   c->pages[b].clear();
   c->pos_h[b] = 0;
+  if (c->cfg.tts_max_tokens) {
+    int off[kTtsCtl] = {};
+    HIPCHECK(hipMemcpy(c->at<int>(c->plan.tts_ctl) + b * kTtsCtl, off, sizeof off, hipMemcpyHostToDevice));
+  }
   int frame[kStreams];
   frame[0] = c->cfg.vocab_text;
   for (int k = 1; k < kStreams; ++k) frame[k] = c->cfg.codebook;
@@ -913,11 +938,12 @@ void reset_conv(moshi_ctx* c, int b) {
   HIPCHECK(hipMemcpy(c->at<int>(c->plan.st_pos) + b, &zero, 4, hipMemcpyHostToDevice));
 }
 
-void check_ids(const int32_t* v, long long n, int stride, int first_slot, const moshi_config& g) {
+void check_ids(const int32_t* v, long long n, int stride, int first_slot, const moshi_config& g, int lo = 0) {
   for (long long i = 0; i < n; ++i) {
     const int slot = first_slot + (int)(i % stride);
     const int hi = slot == 0 ? g.vocab_text : g.codebook;
-    if (v[i] < 0 || v[i] > hi) fail(MOSHI_EINVAL, "token id %d out of range [0, %d] in slot %d", v[i], hi, slot);
+    if (v[i] < lo || v[i] > hi)
+      fail(MOSHI_EINVAL, "token id %d out of range [%d, %d] in slot %d", v[i], lo, hi, slot);
   }
 }
 
@@ -1188,8 +1214,10 @@ int moshi_step(moshi_ctx* c, int32_t B, const int32_t* user, const int32_t* forc
     const bool dev = flags & MOSHI_DEVICE_PTRS;
     if (!dev) {
       check_ids(user, (long long)B * 8, 8, 9, g);
-      if (force) check_ids(force, (long long)B * kSlots, kSlots, 0, g);
+      if (force) check_ids(force, (long long)B * kSlots, kSlots, 0, g, -1);
     }
+    const bool text_only = flags & MOSHI_STEP_TEXT_ONLY;
+    if (text_only && out_audio) fail(MOSHI_EINVAL, "MOSHI_STEP_TEXT_ONLY computes no audio logits");
     order_in(c);
     for (int b = 0; b < B; ++b) ensure_pages(c, b, c->pos_h[b] + 1);
     hipStream_t s = c->stream;
@@ -1207,7 +1235,7 @@ int moshi_step(moshi_ctx* c, int32_t B, const int32_t* user, const int32_t* forc
       HIPCHECK(hipMemcpyAsync(c->ws + p.st_in, c->pin_in, (size_t)(mb * 8 + mb * kSlots + 1) * 4,
                               hipMemcpyHostToDevice, s));
     }
-    run_step(c, B, true);
+    run_step(c, B, !text_only);
     const hipMemcpyKind k = dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
     if (dev) {
       HIPCHECK(hipMemcpyAsync(out_tokens, c->ws + p.st_out_tok, (size_t)B * kSlots * 4, k, s));
@@ -1438,6 +1466,45 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
     HIPCHECK(hipGetLastError());
     *avg_us = ms * 1000.f / iters;
     *bytes_per_launch = bytes;
+  });
+}
+
+int moshi_tts_text(moshi_ctx* c, int32_t conv, const int32_t* tokens, const int32_t* word_lens, int32_t n_words,
+                   int32_t pad_id, int32_t epad_id, float target_pad_ratio, float bonus) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    const moshi_config& g = c->cfg;
+    const Plan& p = c->plan;
+    if (!g.tts_max_tokens) fail(MOSHI_EINVAL, "the context has no TTS text capacity (tts_max_tokens = 0)");
+    if (conv < 0 || conv >= g.max_batch) fail(MOSHI_EINVAL, "conversation %d out of range", conv);
+    if (n_words < 0 || (n_words > 0 && (!tokens || !word_lens))) fail(MOSHI_EINVAL, "bad word list");
+    if (pad_id < 0 || pad_id >= g.vocab_text || epad_id < 0 || epad_id >= g.vocab_text)
+      fail(MOSHI_EINVAL, "PAD and EPAD must be text ids in [0, %d)", g.vocab_text);
+    if (!(bonus >= 0.f) || !std::isfinite(bonus) || !std::isfinite(target_pad_ratio))
+      fail(MOSHI_EINVAL, "the bonus must be finite and >= 0, the target finite");
+    long long n = 0;
+    for (int w = 0; w < n_words; ++w) {
+      if (word_lens[w] < 1) fail(MOSHI_EINVAL, "word %d is empty", w);
+      n += word_lens[w];
+    }
+    if (n > g.tts_max_tokens) fail(MOSHI_EINVAL, "%lld text tokens exceed tts_max_tokens = %d", n, g.tts_max_tokens);
+    std::vector<int32_t> start((size_t)n);
+    for (long long i = 0, w = 0; w < n_words; ++w)
+      for (int k = 0; k < word_lens[w]; ++k, ++i) {
+        if (tokens[i] < 0 || tokens[i] >= g.vocab_text) fail(MOSHI_EINVAL, "text id %d out of range", tokens[i]);
+        start[(size_t)i] = k == 0;
+      }
+    int32_t ctl[kTtsCtl] = {(int32_t)n, 0, 0, 0, pad_id, epad_id, 0, 0};
+    memcpy(&ctl[6], &target_pad_ratio, 4);
+    memcpy(&ctl[7], &bonus, 4);
+    HIPCHECK(hipStreamSynchronize(c->stream));
+    if (n) {
+      HIPCHECK(hipMemcpy(c->at<int>(p.tts_tok) + (size_t)conv * g.tts_max_tokens, tokens, (size_t)n * 4,
+                         hipMemcpyHostToDevice));
+      HIPCHECK(hipMemcpy(c->at<int>(p.tts_start) + (size_t)conv * g.tts_max_tokens, start.data(), (size_t)n * 4,
+                         hipMemcpyHostToDevice));
+    }
+    HIPCHECK(hipMemcpy(c->at<int>(p.tts_ctl) + conv * kTtsCtl, ctl, sizeof ctl, hipMemcpyHostToDevice));
   });
 }
 

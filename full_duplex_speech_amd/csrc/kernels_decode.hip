@@ -1988,6 +1988,33 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
   }
 }
 
+// Zero-shot TTS text control (walkthrough appendix C, TTS mode, Fig. 9): inside
+// a word its next token is fed without consulting the model; otherwise the
+// argmax with a bonus on PAD while the running PAD ratio is under the target
+// decides: PAD or EPAD is kept, any other choice starts the next word (PAD once
+// the text is used up). best/bi: the plain argmax of the logits l.
+__device__ int tts_choose(const ArgmaxArgs& a, int* ctl, const float* l, float best, int bi) {
+  const int b = blockIdx.x;
+  const int n = ctl[0], pad = ctl[4], epad = ctl[5];
+  int cur = ctl[1], n_pad = ctl[2], n_steps = ctl[3];
+  const float target = __int_as_float(ctl[6]), bonus = __int_as_float(ctl[7]);
+  const int* tok = a.tts_tok + (long long)b * a.tts_cap;
+  const int* wstart = a.tts_start + (long long)b * a.tts_cap;
+  int t;
+  if (cur > 0 && cur < n && !wstart[cur]) {
+    t = tok[cur++];
+  } else {
+    if ((float)n_pad < target * (float)max(n_steps, 1)) better(best, bi, l[pad] + bonus, pad);
+    if (bi == pad || bi == epad) t = bi;
+    else if (cur < n) t = tok[cur++];
+    else t = pad;
+  }
+  ctl[1] = cur;
+  ctl[2] = n_pad + (t == pad ? 1 : 0);
+  ctl[3] = n_steps + 1;
+  return t;
+}
+
 __global__ __launch_bounds__(1024) void k_argmax(ArgmaxArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* l = a.logits + (long long)b * a.ld;
@@ -2023,9 +2050,12 @@ __global__ __launch_bounds__(1024) void k_argmax(ArgmaxArgs a) {
   if (tid == 0) {
     for (int w = 1; w < 16; ++w) better(bv, bi, sv[w], si[w]);
     int own = (bi == 0x7fffffff) ? 0 : bi;
-    if (a.pad_after && a.pos[b] < a.delay) own = a.pad_id;
+    int* ctl = a.tts_ctl ? a.tts_ctl + b * kTtsCtl : nullptr;
+    if (ctl && ctl[0] > 0) own = tts_choose(a, ctl, l, bv, own);
+    if (a.pos[b] < a.start) own = a.pad_id;
     a.out_tok[b * kSlots + a.slot] = own;
-    a.cur_tok[b * kSlots + a.slot] = *a.has_force ? a.force[b * kSlots + a.slot] : own;
+    const int f = *a.has_force ? a.force[b * kSlots + a.slot] : -1;
+    a.cur_tok[b * kSlots + a.slot] = f >= 0 ? f : own;
   }
 }
 
@@ -2039,13 +2069,21 @@ __global__ void k_advance(AdvanceArgs a, int B) {
   const int t = threadIdx.x;
   if (t < B * kStreams) {
     const int b = t / kStreams, k = t - b * kStreams;
-    int v = k >= kSlots ? a.user[b * 8 + (k - kSlots)]
-                        : (*a.has_force ? a.force[b * kSlots + k] : a.cur_tok[b * kSlots + k]);
     const int hi = k == 0 ? a.pad_text : a.pad_audio;
+    int v;
+    if (k >= kSlots) {
+      v = a.user[b * 8 + (k - kSlots)];
+    } else {
+      const int f = *a.has_force ? a.force[b * kSlots + k] : -1;
+      if (f >= 0) v = f;
+      else if (a.text_only && k >= 1) v = a.pad_audio;
+      else v = a.cur_tok[b * kSlots + k];
+    }
     if (v < 0 || v > hi) {
       atomicOr(a.err, 1);
       v = hi;
     }
+    if (a.text_only && k >= 1 && k < kSlots) a.out_tok[b * kSlots + k] = v;
     a.prev[b * kStreams + k] = v;
   }
   __syncthreads();

@@ -104,24 +104,34 @@ struct ArgmaxArgs {
   const float* logits;  // [B][ld]
   int n, ld;
   int slot;
-  int pad_after;   // pad the slot while pos[b] < delay (acoustic slots)
-  int pad_id, delay;
+  int start;       // the slot is pad_id while pos[b] < start (its stream has not begun)
+  int pad_id;
   const int* pos;
   int* out_tok;    // [B][9] own tokens
   int* cur_tok;    // [B][9] tokens fed forward (forced or own)
-  const int* force;      // [B][9]
+  const int* force;      // [B][9]; an entry < 0 leaves the slot to the model
   const int* has_force;  // scalar flag
+  // TTS text control of slot 0 (null: off): per conversation kTtsCtl words
+  // {n tokens (0: off), cursor, n_pad, n_steps, pad id, epad id, target bits,
+  // bonus bits} and the text, tokens [cap] and word-start flags [cap]
+  int* tts_ctl;
+  const int* tts_tok;
+  const int* tts_start;
+  int tts_cap;
 };
+constexpr int kTtsCtl = 8;
 
 struct AdvanceArgs {
   const int* cur_tok;  // [B][9]
-  const int* force;      // [B][9], used instead of cur_tok when *has_force
+  const int* force;      // [B][9], entries >= 0 used instead of cur_tok when *has_force
   const int* has_force;
   const int* user;     // [B][8]
   int* prev;           // [B][17]
   int* pos;            // [B]
   int* err;
   int pad_text, pad_audio;
+  int text_only;  // no depth ran: slots 1..8 are forced or pad, also written to out_tok
+  int* out_tok;   // [B][9]
 };
 
 struct CeRowsArgs {

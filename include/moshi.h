@@ -59,6 +59,7 @@ extern "C" {
 #define MOSHI_TF_FILL_KV 2    /* teacher-forced: keep the KV cache and continue
                                  streaming at frame S+1 */
 #define MOSHI_TF_SKIP_DEPTH 4 /* teacher-forced: temporal pass and text only */
+#define MOSHI_STEP_TEXT_ONLY 8 /* moshi_step: skip the Depth Transformer (streaming ASR) */
 
 /* Model and capacity description. Shapes follow [W] "使用 RQ-Transformer ..."
  * (Temporal Transformer with the Helium architecture, Depth Transformer with
@@ -77,6 +78,11 @@ typedef struct moshi_config {
   int32_t page_frames;                       /* KV page size in frames (64) */
   int32_t n_pages;                           /* KV pages in the pool; 0 = max_batch*ceil(ctx_max/page_frames) */
   int32_t max_tf_tokens;                     /* max B*S of moshi_forward_teacher_forced (0 = ctx_max*max_batch) */
+  int32_t text_delay;     /* frames between the text and the audio streams ([W] "推导流式ASR和TTS",
+                             appendix C): > 0 delays the text (streaming ASR, Fig. 8), < 0 delays
+                             every audio stream (streaming TTS, Fig. 9), 0 is the dialogue layout;
+                             |text_delay| < ctx_max */
+  int32_t tts_max_tokens; /* capacity of the per-conversation TTS text (moshi_tts_text); 0 = none */
 } moshi_config;
 
 /* One weight tensor handed to moshi_init_weights: float32, C-order. Names and
@@ -132,7 +138,7 @@ int moshi_init_weights(moshi_ctx* ctx, const moshi_tensor* tensors, int n);
 
 /* Start conversation b afresh (b = -1: all): position 0, previous frame =
  * the all-pad initial frame V_0 ([W] "使用 RQ-Transformer ...": fixed initial
- * token), its KV pages returned to the pool. */
+ * token), its KV pages returned to the pool, its TTS text control switched off. */
 int moshi_reset(moshi_ctx* ctx, int b);
 
 /* One frame for conversations 0..batch-1 ([W] Fig. 4 and the inference
@@ -142,14 +148,45 @@ int moshi_reset(moshi_ctx* ctx, int b);
  *   user_codes [batch][8]: the user's slots 9..16 of this frame (model order).
  *   force [batch][9] or NULL: Moshi's slots 0..8 to use instead of the
  *       model's own as depth inputs and as the stored frame (teacher forcing).
+ *       An entry of -1 leaves that slot to the model, so one modality can be
+ *       forced alone: the audio for streaming ASR ([W] appendix C, ASR mode),
+ *       the text for TTS ([W] Fig. 9), or EPAD to make Moshi start speaking
+ *       ([W] inference paragraph after Fig. 4).
  *   out_tokens [batch][9]: the model's own greedy tokens (argmax, lowest index
- *       on ties); acoustic slots 2..8 are pad while p < delay.
+ *       on ties). A slot is pad before its stream starts: text while
+ *       p < max(text_delay, 0), the semantic codebook while p < max(-text_delay, 0),
+ *       acoustic codebooks 2..8 while p < max(-text_delay, 0) + delay.
+ *       With a TTS text (moshi_tts_text) slot 0 is that control's choice.
  *   out_text_logits [batch][vocab_text], out_audio_logits [batch][8][codebook]:
  *       optional (NULL) float32 logits.
+ *   flags: MOSHI_DEVICE_PTRS; MOSHI_STEP_TEXT_ONLY skips the Depth Transformer
+ *       (streaming ASR discards the model's audio): slots 1..8 of out_tokens
+ *       and of the stored frame are then the forced ids, or pad where force
+ *       is NULL or -1, and out_audio_logits must be NULL.
  * Errors: MOSHI_ECONTEXT if some conversation is at ctx_max; MOSHI_EINVAL for
- * ids outside [0, pad] (with MOSHI_DEVICE_PTRS reported by moshi_sync). */
+ * ids outside [0, pad] (force: [-1, pad]), with MOSHI_DEVICE_PTRS reported by
+ * moshi_sync. */
 int moshi_step(moshi_ctx* ctx, int32_t batch, const int32_t* user_codes, const int32_t* force,
                int32_t* out_tokens, float* out_text_logits, float* out_audio_logits, int32_t flags);
+
+/* Zero-shot TTS text control of conversation `conv` ([W] appendix C, TTS mode and
+ * Fig. 9). From the next step on, the text slot of that conversation is chosen
+ * in the argmax kernel, per step:
+ *   - inside a word (the next text token continues the word being fed): that
+ *     token, without consulting the model;
+ *   - otherwise the argmax of the text logits, with `bonus` added to the PAD logit
+ *     while n_pad < target_pad_ratio * max(n_steps, 1) (float32; n_pad and n_steps
+ *     count the PAD tokens and all tokens chosen so far). PAD or EPAD is kept;
+ *     any other token is replaced by the first token of the next word, or by PAD
+ *     once every word has been fed.
+ * tokens [sum of word_lens]: the text ids of the words in speaking order, in
+ * [0, vocab_text); word_lens [n_words] >= 1; pad_id, epad_id: the vocabulary's PAD
+ * and EPAD ids; bonus >= 0. n_words = 0 switches the control off. A forced text
+ * slot (force[b][0] >= 0) still overrides the choice for the frame it is given.
+ * Host pointers; synchronises the context's stream. MOSHI_EINVAL for a bad
+ * argument or more than tts_max_tokens tokens. */
+int moshi_tts_text(moshi_ctx* ctx, int32_t conv, const int32_t* tokens, const int32_t* word_lens,
+                   int32_t n_words, int32_t pad_id, int32_t epad_id, float target_pad_ratio, float bonus);
 
 /* Teacher-forced pass over tokens [B][S][17] = V_1..V_S in model order
  * (inputs V_0..V_{S-1}, V_0 the pad frame) for conversations 0..B-1, which

@@ -13,8 +13,11 @@ from .moshi_oracle import (  # noqa: F401
     joint_sequence,
     rms_norm,
     rope,
+    shift_stream,
     silu,
+    stream_starts,
     top2_margin,
     undelay_codes,
 )
 from .quant import dequantize_q8, dequantized_weights, is_linear, quantize_q8  # noqa: F401,E402
+from .tts_control import TtsTextControl  # noqa: F401,E402

@@ -9,7 +9,9 @@ Sources (web pages; cited by page and section, equation or figure):
       139.9.1.231 ("论文解读"), sections "Helium 文本语言模型 / 架构",
       "使用 RQ-Transformer 的分层自回归建模" (Fig. 3), "音频建模 / 声学延迟"
       (eq. 4), "多流建模", "内心独白", "Moshi的联合序列建模" (eq. 6, Fig. 4),
-      "训练损失";
+      "训练损失", "推导流式ASR和TTS", the inference paragraph after Fig. 4,
+      and appendix C ("延迟文本语言模型作为zero-shot流式ASR和TTS", Figs. 8
+      and 9);
   [N] the notes page "Moshi: a Speech-Text Foundation Model for Real-Time
       Dialogue", sections 3b (Helium), 3c (multi-stream generation) and 4
       (loss weighting);
@@ -72,19 +74,47 @@ def undelay_codes(model: np.ndarray, tau: int) -> np.ndarray:
     return out
 
 
+def shift_stream(x: np.ndarray, n: int, pad: int) -> np.ndarray:
+    """Delay a stream by n >= 0 steps along its first axis: step s carries
+    x[s - n], and the first n steps (whose sources precede the first frame) are
+    ``pad``."""
+    x = np.asarray(x)
+    out = np.full(x.shape, pad, dtype=x.dtype)
+    for s in range(n, x.shape[0]):
+        out[s] = x[s - n]
+    return out
+
+
+def stream_starts(cfg) -> Tuple[int, int]:
+    """First step at which the text stream and the audio streams carry frame 1.
+
+    [W] "推导流式ASR和TTS" and appendix C: a delay between the text and the
+    audio tokens selects the modality the model conditions on. ASR delays the
+    text behind the audio (Fig. 8), TTS delays the audio behind the text
+    (Fig. 9), both by 2 s (25 frames at 12.5 Hz) with acoustic delay 2.
+    READING: ``cfg.text_delay`` is signed; a positive value delays the text
+    stream by that many steps, a negative one delays every audio stream (Moshi's
+    and the user's) by its magnitude, the acoustic delay applying on top.
+    Returns (text_start, audio_start)."""
+    d = int(getattr(cfg, "text_delay", 0))
+    return max(d, 0), max(-d, 0)
+
+
 def joint_sequence(cfg, text: np.ndarray, moshi: np.ndarray, user: np.ndarray) -> np.ndarray:
     """The joint sequence V[s, k] of [W] "Moshi的联合序列建模" (eq. 6, Fig. 4).
 
     K = 2Q + 1 sub-streams: the text token first ([W] "内心独白": text is the
     prefix of the semantic token), then Moshi's Q codebooks, then the user's Q
     codebooks, each audio stream delayed as in ``delay_codes`` ([W] "多流建模":
-    the delay is applied to both audio streams before concatenation).
+    the delay is applied to both audio streams before concatenation). With a
+    text-audio delay (``stream_starts``) the delayed modality is shifted further.
     """
     T = len(text)
+    t0, a0 = stream_starts(cfg)
     V = np.empty((T, cfg.n_streams), dtype=np.int32)
-    V[:, 0] = text
-    V[:, 1:1 + cfg.n_q] = delay_codes(moshi, cfg.delay, cfg.pad_audio)
-    V[:, 1 + cfg.n_q:] = delay_codes(user, cfg.delay, cfg.pad_audio)
+    V[:, 0] = shift_stream(text, t0, cfg.pad_text)
+    V[:, 1:1 + cfg.n_q] = shift_stream(delay_codes(moshi, cfg.delay, cfg.pad_audio), a0, cfg.pad_audio)
+    V[:, 1 + cfg.n_q:] = shift_stream(delay_codes(user, cfg.delay, cfg.pad_audio), a0, cfg.pad_audio)
     return V
 
 
@@ -336,33 +366,67 @@ class Session:
         self.pos = 0
         self.prev = model.initial_frame.copy()
 
-    def step(self, user_codes: np.ndarray, force: Optional[np.ndarray] = None):
+    def starts(self) -> np.ndarray:
+        """Per own slot (text, semantic, 7 acoustic), the first frame whose source
+        exists: earlier own tokens are pad (``stream_starts``, ``delay_codes``)."""
+        cfg = self.m.cfg
+        t0, a0 = stream_starts(cfg)
+        return np.array([t0, a0] + [a0 + cfg.delay] * (cfg.n_q - 1))
+
+    def step(self, user_codes: np.ndarray, force: Optional[np.ndarray] = None, text_only: bool = False,
+             text_choice=None):
         """Advance one frame. ``user_codes`` are the user's n_q sub-streams of this
         frame in model (delayed) order. ``force`` (optional, n_q + 1 ids) replaces
-        the model's own tokens as depth inputs and as the stored frame.
+        the model's own tokens as depth inputs and as the stored frame; an entry
+        of -1 leaves that slot to the model. This is the control the pages
+        describe: ASR forces the audio and samples the text ([W] appendix C, ASR
+        mode), TTS forces the text ([W] Fig. 9), and forcing EPAD makes Moshi
+        start speaking ([W] inference paragraph after Fig. 4).
+
+        ``text_only`` skips the Depth Transformer. Streaming ASR discards the
+        model's audio predictions, so the depth is not run. The own audio tokens
+        are then the forced ones, or pad where a slot is not forced, and the
+        returned audio logits are None.
+
+        ``text_choice`` (optional) replaces the argmax of the text slot: it is
+        called with the text logits and returns the token (the TTS text control
+        of ``oracle.tts_control``).
 
         Returns (own tokens [n_q+1], text logits [vocab_text], audio logits
-        [n_q, codebook]). At frames s < delay the acoustic codebooks are pad:
-        their sources precede the first codec frame (``delay_codes``).
+        [n_q, codebook]). Own tokens of a slot whose stream has not started are
+        pad (``starts``).
         """
         m, cfg = self.m, self.m.cfg
         if self.pos + 1 > cfg.ctx_max:
             raise ValueError("context overflow")
+        st = self.starts()
+        forced = (lambda k: force is not None and int(force[k]) >= 0)
         z, lt = m.temporal(self.prev[None, :], self.pos, self.cache)
         own = np.empty(cfg.n_q + 1, dtype=np.int32)
-        own[0] = int(np.argmax(lt[0]))
-        tok = int(force[0]) if force is not None else int(own[0])
-        audio = np.empty((cfg.n_q, cfg.codebook), dtype=m.dt)
-        dcache = m.new_depth_cache(1)
-        for j in range(cfg.n_q):
-            audio[j] = m.depth_position(j, z, np.array([tok]), dcache)[0]
-            t = int(np.argmax(audio[j]))
-            if j >= 1 and self.pos < cfg.delay:
-                t = cfg.pad_audio
-            own[j + 1] = t
-            tok = int(force[j + 1]) if force is not None else t
+        own[0] = int(text_choice(lt[0])) if text_choice is not None else int(np.argmax(lt[0]))
+        if self.pos < st[0]:
+            own[0] = cfg.pad_text
+        fed = own.copy()
+        fed[0] = int(force[0]) if forced(0) else own[0]
+        audio = None
+        if text_only:
+            for j in range(cfg.n_q):
+                own[j + 1] = int(force[j + 1]) if forced(j + 1) else cfg.pad_audio
+                fed[j + 1] = own[j + 1]
+        else:
+            audio = np.empty((cfg.n_q, cfg.codebook), dtype=m.dt)
+            dcache = m.new_depth_cache(1)
+            tok = fed[0]
+            for j in range(cfg.n_q):
+                audio[j] = m.depth_position(j, z, np.array([tok]), dcache)[0]
+                t = int(np.argmax(audio[j]))
+                if self.pos < st[j + 1]:
+                    t = cfg.pad_audio
+                own[j + 1] = t
+                fed[j + 1] = int(force[j + 1]) if forced(j + 1) else t
+                tok = fed[j + 1]
         frame = np.empty(cfg.n_streams, dtype=np.int32)
-        frame[:cfg.n_q + 1] = force if force is not None else own
+        frame[:cfg.n_q + 1] = fed
         frame[cfg.n_q + 1:] = user_codes
         self.prev = frame
         self.pos += 1

@@ -53,6 +53,7 @@ class MoshiConfig:
     codebook: int = 2048
     n_q: int = 8
     delay: int = 1
+    text_delay: int = 0  # > 0: text lags the audio by that many frames (ASR); < 0: audio lags text (TTS)
     rope_base: float = 10000.0
     norm_eps: float = 1e-5
     dtype: str = "f32"  # weight precision: "f32", "bf16" or "q8" (8-bit blocks of the bf16 values)
@@ -62,6 +63,7 @@ class MoshiConfig:
     gen_frames: int = 0
     tf_batch: int = 0
     tf_frames: int = 0
+    mode: str = "dialogue"  # streaming workload: "dialogue", "asr" (audio forced, text only) or "tts"
 
     @property
     def n_streams(self) -> int:
@@ -109,6 +111,29 @@ CONFIGS: Dict[str, MoshiConfig] = {
     "b1_7b_q8": MoshiConfig(
         name="b1_7b_q8", vocab_text=32000, dtype="q8", batch=1, prompt_frames=375,
         gen_frames=250, **_TEMPORAL_7B, **_DEPTH_7B),
+    # streaming ASR and TTS: text and audio 2 s (25 frames) apart, acoustic delay 2
+    "tiny_asr": MoshiConfig(
+        name="tiny_asr", d_t=256, n_layers_t=2, n_heads_t=4, ffn_t=688, ctx_max=64,
+        d_d=128, n_layers_d=2, n_heads_d=4, ffn_d=352, vocab_text=1000, delay=2, text_delay=25,
+        dtype="f32", batch=1, prompt_frames=0, gen_frames=50, mode="asr"),
+    "tiny_tts": MoshiConfig(
+        name="tiny_tts", d_t=256, n_layers_t=2, n_heads_t=4, ffn_t=688, ctx_max=64,
+        d_d=128, n_layers_d=2, n_heads_d=4, ffn_d=352, vocab_text=1000, delay=2, text_delay=-25,
+        dtype="f32", batch=1, prompt_frames=0, gen_frames=50, mode="tts"),
+    "mid_asr": MoshiConfig(
+        name="mid_asr", d_t=1024, n_layers_t=8, n_heads_t=16, ffn_t=2816, ctx_max=4096,
+        vocab_text=32000, delay=2, text_delay=25, dtype="bf16", batch=1, prompt_frames=0,
+        gen_frames=100, mode="asr", **_DEPTH_7B),
+    "mid_tts": MoshiConfig(
+        name="mid_tts", d_t=1024, n_layers_t=8, n_heads_t=16, ffn_t=2816, ctx_max=4096,
+        vocab_text=32000, delay=2, text_delay=-25, dtype="bf16", batch=1, prompt_frames=0,
+        gen_frames=100, mode="tts", **_DEPTH_7B),
+    "b1_7b_asr": MoshiConfig(
+        name="b1_7b_asr", vocab_text=32000, delay=2, text_delay=25, dtype="bf16", batch=1,
+        prompt_frames=375, gen_frames=250, mode="asr", **_TEMPORAL_7B, **_DEPTH_7B),
+    "b1_7b_tts": MoshiConfig(
+        name="b1_7b_tts", vocab_text=32000, delay=2, text_delay=-25, dtype="bf16", batch=1,
+        prompt_frames=375, gen_frames=250, mode="tts", **_TEMPORAL_7B, **_DEPTH_7B),
     # 7B shape, 8 conversations at 5-minute context
     "b8_7b_5min": MoshiConfig(
         name="b8_7b_5min", vocab_text=32000, dtype="bf16", batch=8, prompt_frames=3750,
