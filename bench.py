@@ -5,7 +5,7 @@ prompt prefilled into the KV cache, then 250 greedy frames with new random user
 codes every frame. Prints one JSON line (frames/s, ms per frame, roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample).
 
-    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|mid_bf16|tiny]
+    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|mid_bf16|tiny]
 """
 from __future__ import annotations
 
@@ -92,6 +92,8 @@ def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
         weights = dequantized_weights(weights)
     m = Oracle(cfg, weights, dtype=np.float32)
     sess = Session(m)
+    if cfg.temp_text or cfg.temp_audio:
+        sess.set_sampling(cfg.temp_text, cfg.temp_audio, 2024)
     t0 = time.perf_counter()
     if P:
         z, _ = m.temporal(np.concatenate([m.initial_frame[None], prompts[0][:P - 1]]), 0, sess.cache)
@@ -108,7 +110,7 @@ def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
             sess.step(users[0][P + i], text_choice=ctl.choose if ctl else None)
     dt = time.perf_counter() - t0
     return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": cores, "kind": "oracle",
-            "sample": f"{frames} greedy frames of one conversation at positions {P}..{P + frames - 1} "
+            "sample": f"{frames} generated frames of one conversation at positions {P}..{P + frames - 1} "
                       f"(float32 NumPy oracle; prompt prefill {t_prefill:.1f} s untimed); "
                       f"a batch of {B} costs {B}x on the host",
             "ms_per_frame": round(dt * 1000 / frames, 2)}
@@ -196,6 +198,8 @@ def main():
             if P:
                 pr = np.ascontiguousarray(np.stack([p[:P] for p in prompts]))
                 fds.moshi_forward_teacher_forced(ctx, pr, B, P, fds.MOSHI_TF_FILL_KV | fds.MOSHI_TF_SKIP_DEPTH)
+            if cfg.temp_text or cfg.temp_audio:
+                fds.moshi_set_sampling(ctx, cfg.temp_text, cfg.temp_audio, 2024)
             if cfg.mode == "tts":
                 for b in range(B):
                     fds.moshi_tts_text(ctx, b, tts_words(cfg, b), 0, 1, 0.65, 0.5)
@@ -220,7 +224,9 @@ def main():
         what = {"asr": "streaming ASR (text 2 s behind the audio, audio forced, depth skipped)",
                 "tts": "streaming TTS (audio 2 s behind the text, in-kernel text control)"}.get(cfg.mode,
                                                                                               "streaming decode")
-        workload = {"workload": f"{shape} {what}, batch {B}, {P}-frame prompt then {K} greedy frames"
+        if cfg.temp_text or cfg.temp_audio:
+            what += f" sampled at temperatures {cfg.temp_text} (text) / {cfg.temp_audio} (audio)"
+        workload = {"workload": f"{shape} {what}, batch {B}, {P}-frame prompt then {K} generated frames"
                     if cfg.d_t == 4096 else f"{cfg.name} streaming decode, batch {B}, {P}-frame prompt then "
                     f"{K} greedy frames", "config": cfg.name, "batch": B, "prompt_frames": P, "frames": K}
 

@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     moshi_position,
     moshi_read_q8,
     moshi_tts_text,
+    moshi_set_sampling,
     moshi_reset,
     moshi_step,
     moshi_sync,

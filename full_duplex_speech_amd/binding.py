@@ -60,7 +60,7 @@ EXPORTS = (
     "moshi_workspace_bytes", "moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset",
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
     "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel", "moshi_read_q8",
-    "moshi_tts_text",
+    "moshi_tts_text", "moshi_set_sampling",
 )
 KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5, "tf_gate_up": 6,
            "tf_attn": 7}
@@ -94,11 +94,13 @@ def lib() -> ctypes.CDLL:
     L.moshi_time_kernel.argtypes = [VP, I32, I32, I32, P(ctypes.c_float), P(ctypes.c_double)]
     L.moshi_read_q8.argtypes = [VP, ctypes.c_char_p, VP, VP, VP]
     L.moshi_tts_text.argtypes = [VP, I32, VP, VP, I32, I32, I32, ctypes.c_float, ctypes.c_float]
+    L.moshi_set_sampling.argtypes = [VP, ctypes.c_float, ctypes.c_float, ctypes.c_uint64]
     L.moshi_destroy.argtypes = [VP]
     L.moshi_destroy.restype = None
     for n in ("moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset", "moshi_step",
               "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
-              "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8", "moshi_tts_text"):
+              "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8", "moshi_tts_text",
+              "moshi_set_sampling"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -248,6 +250,10 @@ def moshi_tts_text(ctx, conv: int, words, pad_id: int, epad_id: int, target_pad_
                                      target_pad_ratio, bonus))
 
 
+def moshi_set_sampling(ctx, temp_text: float, temp_audio: float, seed: int) -> None:
+    _check(ctx, lib().moshi_set_sampling(ctx, temp_text, temp_audio, seed))
+
+
 def moshi_last_error(ctx) -> str:
     return lib().moshi_last_error(ctx).decode()
 
@@ -313,6 +319,9 @@ class Moshi:
         la = np.empty((B, cfg.n_q, cfg.codebook), dtype=np.float32) if logits and not text_only else None
         moshi_step(self.ctx, B, u, f, tok, lt, la, MOSHI_STEP_TEXT_ONLY if text_only else 0)
         return tok, lt, la
+
+    def set_sampling(self, temp_text: float, temp_audio: float, seed: int) -> None:
+        moshi_set_sampling(self.ctx, temp_text, temp_audio, seed)
 
     def tts_text(self, words, pad_id: int, epad_id: int, target_pad_ratio: float, bonus: float, conv: int = 0):
         moshi_tts_text(self.ctx, conv, words, pad_id, epad_id, target_pad_ratio, bonus)

@@ -96,6 +96,7 @@ struct Plan {
   // TTS text control: per conversation kTtsCtl words of state (zeroed with the
   // step state: off), then the text and its word-start flags
   size_t tts_ctl = 0, tts_tok = 0, tts_start = 0;
+  size_t st_samp = 0;  // sampling temperatures and seed (zeroed: greedy)
   size_t st_user = 0, st_force = 0, st_has_force = 0;
   // activations (float32)
   size_t h = 0, q = 0, attn = 0, inter = 0, inter16 = 0, dinter16 = 0, part_t = 0, text_logits = 0;
@@ -224,6 +225,7 @@ Plan make_plan(const moshi_config& c) {
   p.st_cnt_t = p.take(mb * c.n_heads_t * 4);
   p.st_cnt_d = p.take(mb * c.n_heads_d * 4);
   if (c.tts_max_tokens) p.tts_ctl = p.take(mb * kTtsCtl * 4);
+  p.st_samp = p.take(4 * 4);
   p.st_end = p.total;
   if (c.tts_max_tokens) {
     p.tts_tok = p.take((size_t)mb * c.tts_max_tokens * 4);
@@ -546,6 +548,7 @@ ArgmaxArgs argmax_args(moshi_ctx* c, int slot) {
   const int text_start = std::max(g.text_delay, 0), audio_start = std::max(-g.text_delay, 0);
   m.start = slot == 0 ? text_start : (slot == 1 ? audio_start : audio_start + g.delay);
   m.pad_id = slot == 0 ? g.vocab_text : g.codebook;
+  m.samp = c->at<int>(p.st_samp);
   if (slot == 0 && g.tts_max_tokens) {
     m.tts_ctl = c->at<int>(p.tts_ctl);
     m.tts_tok = c->at<int>(p.tts_tok);
@@ -1466,6 +1469,21 @@ int moshi_time_kernel(moshi_ctx* c, int32_t kernel, int32_t batch, int32_t iters
     HIPCHECK(hipGetLastError());
     *avg_us = ms * 1000.f / iters;
     *bytes_per_launch = bytes;
+  });
+}
+
+int moshi_set_sampling(moshi_ctx* c, float temp_text, float temp_audio, uint64_t seed) {
+  if (!c) return MOSHI_EINVAL;
+  return guard_impl(c, [&] {
+    if (!(temp_text >= 0.f) || !(temp_audio >= 0.f) || !std::isfinite(temp_text) || !std::isfinite(temp_audio))
+      fail(MOSHI_EINVAL, "temperatures must be finite and >= 0");
+    int32_t w[4];
+    memcpy(&w[0], &temp_text, 4);
+    memcpy(&w[1], &temp_audio, 4);
+    w[2] = (int32_t)(uint32_t)(seed & 0xffffffffu);
+    w[3] = (int32_t)(uint32_t)(seed >> 32);
+    HIPCHECK(hipStreamSynchronize(c->stream));
+    HIPCHECK(hipMemcpy(c->ws + c->plan.st_samp, w, sizeof w, hipMemcpyHostToDevice));
   });
 }
 

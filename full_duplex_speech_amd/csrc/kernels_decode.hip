@@ -1988,12 +1988,61 @@ __device__ __forceinline__ void better(float& bv, int& bi, float ov, int oi) {
   }
 }
 
+// Counter-based generator for temperature sampling: Philox4x64-10 (Salmon et
+// al., "Parallel random numbers: as easy as 1, 2, 3", SC'11), ten rounds of two
+// 64 x 64 -> 128-bit products with the key bumped by Weyl constants in between.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(c[0], M0), lo0 = c[0] * M0;
+    const uint64_t hi1 = __umul64hi(c[2], M1), lo1 = c[2] * M1;
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+// Gumbel noise -log(-log u) of a generator word: u = (2 (x >> 41) + 1) 2^-24,
+// exact in float32 and inside (0, 1)
+__device__ __forceinline__ float gumbel_of(uint64_t x) {
+  const float u = (float)(2u * (uint32_t)(x >> 41) + 1u) * 0x1p-24f;
+  return -logf(-logf(u));
+}
+
+struct Sampler {
+  float temp;
+  uint64_t seed;
+};
+__device__ __forceinline__ Sampler sampler_of(const ArgmaxArgs& a) {
+  Sampler s{0.f, 0};
+  if (a.samp) {
+    s.temp = __int_as_float(a.samp[a.slot == 0 ? 0 : 1]);
+    s.seed = (uint64_t)(uint32_t)a.samp[2] | ((uint64_t)(uint32_t)a.samp[3] << 32);
+  }
+  return s;
+}
+// the noise of element i of a draw: counter (i / 4, position, conversation,
+// slot), word i % 4, key (seed, 0)
+__device__ __forceinline__ float gumbel_at(int i, int pos, int b, int slot, uint64_t seed) {
+  uint64_t c[4] = {(uint64_t)(i >> 2), (uint64_t)pos, (uint64_t)b, (uint64_t)slot};
+  philox4x64_10(c, seed, 0);
+  return gumbel_of(c[i & 3]);
+}
+
 // Zero-shot TTS text control (walkthrough appendix C, TTS mode, Fig. 9): inside
 // a word its next token is fed without consulting the model; otherwise the
 // argmax with a bonus on PAD while the running PAD ratio is under the target
 // decides: PAD or EPAD is kept, any other choice starts the next word (PAD once
 // the text is used up). best/bi: the plain argmax of the logits l.
-__device__ int tts_choose(const ArgmaxArgs& a, int* ctl, const float* l, float best, int bi) {
+__device__ int tts_choose(const ArgmaxArgs& a, int* ctl, const float* l, float best, int bi, Sampler sm) {
   const int b = blockIdx.x;
   const int n = ctl[0], pad = ctl[4], epad = ctl[5];
   int cur = ctl[1], n_pad = ctl[2], n_steps = ctl[3];
@@ -2004,7 +2053,13 @@ __device__ int tts_choose(const ArgmaxArgs& a, int* ctl, const float* l, float b
   if (cur > 0 && cur < n && !wstart[cur]) {
     t = tok[cur++];
   } else {
-    if ((float)n_pad < target * (float)max(n_steps, 1)) better(best, bi, l[pad] + bonus, pad);
+    if ((float)n_pad < target * (float)max(n_steps, 1)) {
+      // PAD's score with the bonus on its logit (the bonus is >= 0, so comparing
+      // it with the block's best is the argmax over the boosted logits)
+      const float boosted = l[pad] + bonus;
+      const float score = sm.temp > 0.f ? boosted / sm.temp + gumbel_at(pad, a.pos[b], b, 0, sm.seed) : boosted;
+      better(best, bi, score, pad);
+    }
     if (bi == pad || bi == epad) t = bi;
     else if (cur < n) t = tok[cur++];
     else t = pad;
@@ -2020,9 +2075,31 @@ __global__ __launch_bounds__(1024) void k_argmax(ArgmaxArgs a) {
   const float* l = a.logits + (long long)b * a.ld;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  // 8 independent loads in flight per thread; indices increase within a thread,
-  // so a strict '>' keeps the lowest index of equal values
-  for (int base = 0; base < a.n; base += 1024 * 8) {
+  const Sampler sm = sampler_of(a);
+  // indices increase within a thread, so a strict '>' keeps the lowest index of
+  // equal values
+  if (sm.temp > 0.f) {
+    // temperature draw, Gumbel-max form: argmax of l / T + Gumbel noise; a thread
+    // takes the 4 elements of one generator block at a time
+    const int pos = a.pos[b];
+    for (int g4 = tid; g4 * 4 < a.n; g4 += 1024) {
+      uint64_t c[4] = {(uint64_t)g4, (uint64_t)pos, (uint64_t)b, (uint64_t)a.slot};
+      philox4x64_10(c, sm.seed, 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int i = g4 * 4 + w;
+        if (i < a.n) {
+          const float v = l[i] / sm.temp + gumbel_of(c[w]);
+          if (v > bv) {
+            bv = v;
+            bi = i;
+          }
+        }
+      }
+    }
+  }
+  // greedy: 8 independent loads in flight per thread
+  for (int base = 0; sm.temp <= 0.f && base < a.n; base += 1024 * 8) {
     float v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -2051,7 +2128,7 @@ __global__ __launch_bounds__(1024) void k_argmax(ArgmaxArgs a) {
     for (int w = 1; w < 16; ++w) better(bv, bi, sv[w], si[w]);
     int own = (bi == 0x7fffffff) ? 0 : bi;
     int* ctl = a.tts_ctl ? a.tts_ctl + b * kTtsCtl : nullptr;
-    if (ctl && ctl[0] > 0) own = tts_choose(a, ctl, l, bv, own);
+    if (ctl && ctl[0] > 0) own = tts_choose(a, ctl, l, bv, own, sm);
     if (a.pos[b] < a.start) own = a.pad_id;
     a.out_tok[b * kSlots + a.slot] = own;
     const int f = *a.has_force ? a.force[b * kSlots + a.slot] : -1;

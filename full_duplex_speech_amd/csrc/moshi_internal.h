@@ -118,6 +118,9 @@ struct ArgmaxArgs {
   const int* tts_tok;
   const int* tts_start;
   int tts_cap;
+  // temperature sampling: {text temperature, audio temperature} as float bits,
+  // then the 64-bit seed (low, high word); temperature 0 = greedy
+  const int* samp;
 };
 constexpr int kTtsCtl = 8;
 

@@ -152,8 +152,8 @@ int moshi_reset(moshi_ctx* ctx, int b);
  *       forced alone: the audio for streaming ASR ([W] appendix C, ASR mode),
  *       the text for TTS ([W] Fig. 9), or EPAD to make Moshi start speaking
  *       ([W] inference paragraph after Fig. 4).
- *   out_tokens [batch][9]: the model's own greedy tokens (argmax, lowest index
- *       on ties). A slot is pad before its stream starts: text while
+ *   out_tokens [batch][9]: the model's own tokens: greedy (argmax, lowest index
+ *       on ties) or temperature draws (moshi_set_sampling). A slot is pad before its stream starts: text while
  *       p < max(text_delay, 0), the semantic codebook while p < max(-text_delay, 0),
  *       acoustic codebooks 2..8 while p < max(-text_delay, 0) + delay.
  *       With a TTS text (moshi_tts_text) slot 0 is that control's choice.
@@ -168,6 +168,20 @@ int moshi_reset(moshi_ctx* ctx, int b);
  * moshi_sync. */
 int moshi_step(moshi_ctx* ctx, int32_t batch, const int32_t* user_codes, const int32_t* force,
                int32_t* out_tokens, float* out_text_logits, float* out_audio_logits, int32_t flags);
+
+/* Temperature sampling of the own tokens of every later step (all conversations):
+ * the text slot at temp_text, Moshi's codebooks at temp_audio; 0 = greedy (the
+ * default). The pages sample at 0.6 (streaming TTS) and 0.8 (walkthrough, ASR/TTS
+ * metrics paragraph after Table 9; audio-quality results of the quantisation
+ * section); they fix no generator, so the draw is defined here:
+ *   token = argmax_i (l_i / T + g_i) (lowest index on ties), g_i = -log(-log u_i),
+ *   u_i = (2 (x >> 41) + 1) * 2^-24 with x word i % 4 of Philox4x64-10 (Salmon et
+ *   al., SC'11) under key (seed, 0) at counter (i / 4, position, conversation,
+ *   slot), slot 0 = text, 1..8 = codebooks; float32 arithmetic.
+ * With a TTS text the PAD bonus is added to PAD's logit before the division by T.
+ * Synchronises the context's stream. MOSHI_EINVAL for a negative or non-finite
+ * temperature. */
+int moshi_set_sampling(moshi_ctx* ctx, float temp_text, float temp_audio, uint64_t seed);
 
 /* Zero-shot TTS text control of conversation `conv` ([W] appendix C, TTS mode and
  * Fig. 9). From the next step on, the text slot of that conversation is chosen

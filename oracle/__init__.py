@@ -21,3 +21,4 @@ from .moshi_oracle import (  # noqa: F401
 )
 from .quant import dequantize_q8, dequantized_weights, is_linear, quantize_q8  # noqa: F401,E402
 from .tts_control import TtsTextControl  # noqa: F401,E402
+from . import sampling  # noqa: F401,E402

@@ -360,11 +360,25 @@ class Session:
     and the model's predictions for them are not used). Decoding is greedy:
     argmax, the lowest index winning ties."""
 
-    def __init__(self, model: Oracle):
+    def __init__(self, model: Oracle, conversation: int = 0):
         self.m = model
         self.cache = model.new_temporal_cache()
         self.pos = 0
         self.prev = model.initial_frame.copy()
+        self.conversation = conversation
+        self.temps = (0.0, 0.0)
+        self.seed = 0
+
+    def set_sampling(self, temp_text: float, temp_audio: float, seed: int):
+        """Temperature sampling of the own tokens (``oracle.sampling``); 0 = greedy."""
+        self.temps = (float(temp_text), float(temp_audio))
+        self.seed = int(seed)
+
+    def pick(self, logits: np.ndarray, slot: int) -> int:
+        """The own token of ``slot`` (0 text, 1..8 Moshi's codebooks) at this step."""
+        from .sampling import sample
+        t = self.temps[0] if slot == 0 else self.temps[1]
+        return sample(logits, t, self.seed, self.pos, self.conversation, slot)
 
     def starts(self) -> np.ndarray:
         """Per own slot (text, semantic, 7 acoustic), the first frame whose source
@@ -388,9 +402,10 @@ class Session:
         are then the forced ones, or pad where a slot is not forced, and the
         returned audio logits are None.
 
-        ``text_choice`` (optional) replaces the argmax of the text slot: it is
-        called with the text logits and returns the token (the TTS text control
-        of ``oracle.tts_control``).
+        ``text_choice`` (optional) replaces the draw of the text slot: it is
+        called with the text logits and the sampler and returns the token (the
+        TTS text control of ``oracle.tts_control``). Own tokens are greedy unless
+        ``set_sampling`` chose temperatures.
 
         Returns (own tokens [n_q+1], text logits [vocab_text], audio logits
         [n_q, codebook]). Own tokens of a slot whose stream has not started are
@@ -403,7 +418,8 @@ class Session:
         forced = (lambda k: force is not None and int(force[k]) >= 0)
         z, lt = m.temporal(self.prev[None, :], self.pos, self.cache)
         own = np.empty(cfg.n_q + 1, dtype=np.int32)
-        own[0] = int(text_choice(lt[0])) if text_choice is not None else int(np.argmax(lt[0]))
+        pick_text = (lambda lg: self.pick(lg, 0))
+        own[0] = int(text_choice(lt[0], pick_text)) if text_choice is not None else pick_text(lt[0])
         if self.pos < st[0]:
             own[0] = cfg.pad_text
         fed = own.copy()
@@ -419,7 +435,7 @@ class Session:
             tok = fed[0]
             for j in range(cfg.n_q):
                 audio[j] = m.depth_position(j, z, np.array([tok]), dcache)[0]
-                t = int(np.argmax(audio[j]))
+                t = self.pick(audio[j], j + 1)
                 if self.pos < st[j + 1]:
                     t = cfg.pad_audio
                 own[j + 1] = t

@@ -23,8 +23,9 @@ READINGS (the page gives the rule, not its arithmetic):
   * the bonus is added to the PAD logit only. A bonus on EPAD would start the
     next word sooner, the opposite of slowing down;
   * once every word has been fed, the controller keeps answering PAD;
-  * the decision is an argmax, lowest index first on ties (decoding is greedy
-    here; the pages' 0.6 temperature belongs to sampling, which is not built),
+  * the decision is the step's draw from the boosted logits: the argmax (lowest
+    index first on ties) when decoding greedily, the temperature draw of
+    ``oracle.sampling`` otherwise (the pages sample TTS at temperature 0.6),
     computed in the precision of the logits it is given.
 """
 from __future__ import annotations
@@ -57,13 +58,15 @@ class TtsTextControl:
         self.n_pad = 0
         self.n_steps = 0
 
-    def choose(self, logits: np.ndarray) -> int:
-        tok = self._decide(np.asarray(logits))
+    def choose(self, logits: np.ndarray, pick=None) -> int:
+        """The text token of one step. ``pick`` maps the (PAD-boosted) logits to a
+        token; the default is the greedy argmax (``Session`` passes its sampler)."""
+        tok = self._decide(np.asarray(logits), pick or (lambda lg: int(np.argmax(lg))))
         self.n_steps += 1
         self.n_pad += int(tok == self.pad_id)
         return tok
 
-    def _decide(self, logits: np.ndarray) -> int:
+    def _decide(self, logits: np.ndarray, pick) -> int:
         n = len(self.tokens)
         # inside a word: its next token, without consulting the model
         if 0 < self.cursor < n and not self.word_start[self.cursor]:
@@ -72,7 +75,7 @@ class TtsTextControl:
         lg = logits.copy()
         if self.below_target():
             lg[self.pad_id] = lg[self.pad_id] + lg.dtype.type(self.bonus)
-        choice = int(np.argmax(lg))
+        choice = int(pick(lg))
         if choice in (self.pad_id, self.epad_id):
             return choice
         if self.cursor < n:

@@ -64,6 +64,8 @@ class MoshiConfig:
     tf_batch: int = 0
     tf_frames: int = 0
     mode: str = "dialogue"  # streaming workload: "dialogue", "asr" (audio forced, text only) or "tts"
+    temp_text: float = 0.0   # sampling temperatures of the own tokens (0 = greedy)
+    temp_audio: float = 0.0
 
     @property
     def n_streams(self) -> int:
@@ -111,6 +113,10 @@ CONFIGS: Dict[str, MoshiConfig] = {
     "b1_7b_q8": MoshiConfig(
         name="b1_7b_q8", vocab_text=32000, dtype="q8", batch=1, prompt_frames=375,
         gen_frames=250, **_TEMPORAL_7B, **_DEPTH_7B),
+    # the batch-1 workload with temperature sampling (text 0.7, audio 0.8)
+    "b1_7b_sampled": MoshiConfig(
+        name="b1_7b_sampled", vocab_text=32000, dtype="bf16", batch=1, prompt_frames=375,
+        gen_frames=250, temp_text=0.7, temp_audio=0.8, **_TEMPORAL_7B, **_DEPTH_7B),
     # streaming ASR and TTS: text and audio 2 s (25 frames) apart, acoustic delay 2
     "tiny_asr": MoshiConfig(
         name="tiny_asr", d_t=256, n_layers_t=2, n_heads_t=4, ffn_t=688, ctx_max=64,
