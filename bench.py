@@ -106,6 +106,8 @@ def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
         if cfg.mode == "asr":
             force = np.concatenate([[-1], prompts[0][P + i, 1:9]])
             sess.step(users[0][P + i], force=force, text_only=True)
+        elif cfg.n_depth == 16:
+            sess.step(None)
         else:
             sess.step(users[0][P + i], text_choice=ctl.choose if ctl else None)
     dt = time.perf_counter() - t0
@@ -181,9 +183,11 @@ def main():
         prompts = [joint_prompt(fds, cfg, b, n_total) for b in range(B)]
         users = [p[:, 9:] for p in prompts]
         user_dev = torch.from_numpy(np.stack([users[b][P:P + max(K, W)] for b in range(B)], axis=1).copy()).cuda()
-        out_dev = torch.empty((max(K, W), B, 9), dtype=torch.int32, device="cuda")
         flags = fds.MOSHI_DEVICE_PTRS
         force_dev = [None] * max(K, W)
+        # a simulated dialogue: the 16-index depth draws the user's codes, none are given
+        user_in = [None if cfg.n_depth == 16 else user_dev[i] for i in range(max(K, W))]
+        out_dev = torch.empty((max(K, W), B, 17 if cfg.n_depth == 16 else 9), dtype=torch.int32, device="cuda")
         if cfg.mode == "asr":
             # streaming ASR: Moshi's audio is forced from the input, the text is free, no depth
             f = np.stack([prompts[b][P:P + max(K, W)] for b in range(B)], axis=1)[..., :9].copy()
@@ -208,13 +212,13 @@ def main():
         prefill()
         log(f"prefill {B} x {P} frames in {time.perf_counter() - t0:.2f} s")
         for i in range(W):
-            fds.moshi_step(ctx, B, user_dev[i], force_dev[i], out_dev[i], None, None, flags)
+            fds.moshi_step(ctx, B, user_in[i], force_dev[i], out_dev[i], None, None, flags)
         fds.moshi_sync(ctx)
         prefill()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            fds.moshi_step(ctx, B, user_dev[i], force_dev[i], out_dev[i], None, None, flags)
+            fds.moshi_step(ctx, B, user_in[i], force_dev[i], out_dev[i], None, None, flags)
         fds.moshi_sync(ctx)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
@@ -224,6 +228,8 @@ def main():
         what = {"asr": "streaming ASR (text 2 s behind the audio, audio forced, depth skipped)",
                 "tts": "streaming TTS (audio 2 s behind the text, in-kernel text control)"}.get(cfg.mode,
                                                                                               "streaming decode")
+        if cfg.n_depth == 16:
+            what = "simulated dialogue (16-index depth draws both speakers)"
         if cfg.temp_text or cfg.temp_audio:
             what += f" sampled at temperatures {cfg.temp_text} (text) / {cfg.temp_audio} (audio)"
         workload = {"workload": f"{shape} {what}, batch {B}, {P}-frame prompt then {K} generated frames"
@@ -270,7 +276,7 @@ def main():
         esz = 2 if cfg.dtype in ("bf16", "q8") else 4
         lin_esz = 1.125 if cfg.dtype == "q8" else esz
         lin = param_count(cfg) - (cfg.vocab_text + 1 + 16 * (cfg.codebook + 1)) * cfg.d_t \
-            - (cfg.vocab_text + 1 + 7 * (cfg.codebook + 1)) * cfg.d_d
+            - (cfg.vocab_text + 1 + (cfg.n_depth - 1) * (cfg.codebook + 1)) * cfg.d_d
         if cfg.mode == "asr":  # no depth: the temporal layers, the norms and the text head only
             lin = cfg.n_layers_t * (4 * cfg.d_t ** 2 + 3 * cfg.d_t * cfg.ffn_t + 2 * cfg.d_t) \
                 + cfg.vocab_text * cfg.d_t + cfg.d_t

@@ -43,7 +43,7 @@ class moshi_config(ctypes.Structure):
                                                "vocab_text", "codebook", "n_q", "delay")] + \
                [("rope_base", ctypes.c_float), ("norm_eps", ctypes.c_float)] + \
                [(n, ctypes.c_int32) for n in ("dtype", "max_batch", "page_frames", "n_pages", "max_tf_tokens",
-                                              "text_delay", "tts_max_tokens")]
+                                              "text_delay", "tts_max_tokens", "n_depth")]
 
 
 class moshi_tensor(ctypes.Structure):
@@ -143,6 +143,7 @@ def config_struct(cfg, max_batch: Optional[int] = None, page_frames: int = 64, n
     c.max_tf_tokens = max_tf_tokens
     c.text_delay = int(getattr(cfg, "text_delay", 0))
     c.tts_max_tokens = tts_max_tokens
+    c.n_depth = int(getattr(cfg, "n_depth", 8))
     return c
 
 
@@ -308,15 +309,21 @@ class Moshi:
 
     def step(self, user_codes: np.ndarray, force: Optional[np.ndarray] = None, logits: bool = False,
              text_only: bool = False):
-        """Host-pointer step: returns (tokens [B, 9], text_logits, audio_logits).
-        ``force`` entries of -1 leave a slot to the model; ``text_only`` skips the depth."""
+        """Host-pointer step: returns (tokens [B, 9] or [B, 17] with a 16-index depth,
+        text_logits, audio_logits). ``force`` entries of -1 leave a slot to the model;
+        ``text_only`` skips the depth; ``user_codes`` may be an int B (no user input:
+        a 16-index depth draws the user's codes)."""
         cfg = self.cfg
-        u = np.ascontiguousarray(user_codes, dtype=np.int32).reshape(-1, 8)
-        B = u.shape[0]
+        nd = 16 if getattr(cfg, "n_depth", 8) == 16 else 8
+        if isinstance(user_codes, (int, np.integer)):
+            u, B = None, int(user_codes)
+        else:
+            u = np.ascontiguousarray(user_codes, dtype=np.int32).reshape(-1, 8)
+            B = u.shape[0]
         f = None if force is None else np.ascontiguousarray(force, dtype=np.int32).reshape(B, 9)
-        tok = np.empty((B, 9), dtype=np.int32)
+        tok = np.empty((B, 17 if nd == 16 else 9), dtype=np.int32)
         lt = np.empty((B, cfg.vocab_text), dtype=np.float32) if logits else None
-        la = np.empty((B, cfg.n_q, cfg.codebook), dtype=np.float32) if logits and not text_only else None
+        la = np.empty((B, nd, cfg.codebook), dtype=np.float32) if logits and not text_only else None
         moshi_step(self.ctx, B, u, f, tok, lt, la, MOSHI_STEP_TEXT_ONLY if text_only else 0)
         return tok, lt, la
 

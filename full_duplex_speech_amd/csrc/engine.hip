@@ -97,6 +97,7 @@ struct Plan {
   // step state: off), then the text and its word-start flags
   size_t tts_ctl = 0, tts_tok = 0, tts_start = 0;
   size_t st_samp = 0;  // sampling temperatures and seed (zeroed: greedy)
+  size_t st_user_own = 0, st_user_cur = 0, st_user_given = 0;
   size_t st_user = 0, st_force = 0, st_has_force = 0;
   // activations (float32)
   size_t h = 0, q = 0, attn = 0, inter = 0, inter16 = 0, dinter16 = 0, part_t = 0, text_logits = 0;
@@ -112,6 +113,10 @@ struct Plan {
   size_t tf_U = 0, tf_Xd = 0, tf_DQ = 0, tf_DK = 0, tf_DV = 0, tf_DO = 0, tf_DI = 0, tf_audio = 0;
   size_t staging = 0, staging_bytes = 0;
 };
+
+// depth indices: Moshi's 8 codebooks, or 16 when the depth also predicts the
+// user's (simulated dialogues)
+int depth_indices(const moshi_config& c) { return c.n_depth == 16 ? 16 : 8; }
 
 int validate(const moshi_config& c, std::string& msg) {
   auto bad = [&](const char* m) {
@@ -132,6 +137,7 @@ int validate(const moshi_config& c, std::string& msg) {
   if (c.delay < 0) return bad("delay must be >= 0");
   if (c.text_delay <= -c.ctx_max || c.text_delay >= c.ctx_max) return bad("|text_delay| must be below ctx_max");
   if (c.tts_max_tokens < 0 || c.tts_max_tokens > (1 << 24)) return bad("tts_max_tokens must be in 0..2^24");
+  if (c.n_depth != 0 && c.n_depth != 8 && c.n_depth != 16) return bad("n_depth must be 0, 8 or 16");
   if (!(c.rope_base > 0.f) || !(c.norm_eps > 0.f)) return bad("rope_base and norm_eps must be positive");
   if (c.dtype != MOSHI_F32 && c.dtype != MOSHI_BF16 && c.dtype != MOSHI_Q8)
     return bad("dtype must be MOSHI_F32, MOSHI_BF16 or MOSHI_Q8");
@@ -173,7 +179,7 @@ Plan make_plan(const moshi_config& c) {
   }
   p.out_norm = p.take(d * 4);
   p.text_head = p.take((long long)c.vocab_text * d * e);
-  for (int j = 0; j < c.n_q; ++j) {
+  for (int j = 0; j < depth_indices(c); ++j) {
     DepthW w;
     w.in_proj = p.take(dd * d * e);
     w.emb = p.take((long long)((j == 0 ? c.vocab_text : c.codebook) + 1) * dd * e);
@@ -200,14 +206,14 @@ Plan make_plan(const moshi_config& c) {
   p.meta_rows = p.take(kStreams * 4);
   const int hdt = c.d_t / c.n_heads_t, hdd = c.d_d / c.n_heads_d;
   p.rope_t = p.take((size_t)c.ctx_max * hdt * 4);
-  p.rope_d = p.take((size_t)c.n_q * hdd * 4);
+  p.rope_d = p.take((size_t)depth_indices(c) * hdd * 4);
   // paged temporal KV (bf16 for bf16 models), flat depth KV (float32)
   p.max_pages_conv = (c.ctx_max + c.page_frames - 1) / c.page_frames;
   p.n_pages = c.n_pages ? c.n_pages : c.max_batch * p.max_pages_conv;
   p.page_elems = (long long)c.n_layers_t * 2 * c.d_t * c.page_frames;
   p.kv_pages = p.take((size_t)p.n_pages * p.page_elems * e);
   p.page_table = p.take((size_t)c.max_batch * p.max_pages_conv * 4);
-  p.depth_kv_elems = (long long)c.n_layers_d * 2 * c.d_d * c.n_q;
+  p.depth_kv_elems = (long long)c.n_layers_d * 2 * c.d_d * depth_indices(c);
   p.depth_kv = p.take((size_t)c.max_batch * p.depth_kv_elems * 4);
   // attention splits: every split covers at most 512 keys at full context
   p.max_splits = (c.ctx_max + 511) / 512;
@@ -226,6 +232,11 @@ Plan make_plan(const moshi_config& c) {
   p.st_cnt_d = p.take(mb * c.n_heads_d * 4);
   if (c.tts_max_tokens) p.tts_ctl = p.take(mb * kTtsCtl * 4);
   p.st_samp = p.take(4 * 4);
+  // 16-index depth: the user's own draws, the user tokens fed forward (given or
+  // own), and whether this step's user codes were given
+  p.st_user_own = p.take(mb * 8 * 4);
+  p.st_user_cur = p.take(mb * 8 * 4);
+  p.st_user_given = p.take(4);
   p.st_end = p.total;
   if (c.tts_max_tokens) {
     p.tts_tok = p.take((size_t)mb * c.tts_max_tokens * 4);
@@ -249,7 +260,7 @@ Plan make_plan(const moshi_config& c) {
   p.dinter = p.take(mb * Fd * 4);
   p.dinter16 = p.take(mb * Fd * 2);
   p.part_d = p.take((size_t)mb * c.n_heads_d * (hdd + 2) * 4);
-  p.audio_logits = p.take((size_t)mb * c.n_q * c.codebook * 4);
+  p.audio_logits = p.take((size_t)mb * depth_indices(c) * c.codebook * 4);
   // teacher-forced
   const long long tf = c.max_tf_tokens ? c.max_tf_tokens : (long long)c.ctx_max * mb;
   p.tf_tokens = p.take((size_t)tf * kStreams * 4);
@@ -353,7 +364,7 @@ void build_dests(moshi_ctx* c) {
   for (int l = 0; l < g.n_layers_t; ++l) layer("temporal.layers." + std::to_string(l) + ".", p.lt[l], d, g.ffn_t);
   add_dest(c, "temporal.out_norm", p.out_norm, 1, (int)d, 1, 0, true);
   add_dest(c, "temporal.text_head", p.text_head, g.vocab_text, (int)d);
-  for (int j = 0; j < g.n_q; ++j) {
+  for (int j = 0; j < depth_indices(g); ++j) {
     const std::string pre = "depth." + std::to_string(j) + ".";
     const DepthW& w = p.dj[j];
     add_dest(c, pre + "in_proj", w.in_proj, dd, (int)d);
@@ -398,7 +409,7 @@ KvView depth_kv(moshi_ctx* c) {
   v.page_table = nullptr;
   v.pt_stride = 0;
   v.page_stride = c->plan.depth_kv_elems;
-  v.pf = g.n_q;
+  v.pf = depth_indices(g);
   v.n_heads = g.n_heads_d;
   v.hd = g.d_d / g.n_heads_d;
   return v;
@@ -455,7 +466,7 @@ AttnArgs attn_args(moshi_ctx* c, int layer, bool depth_model, int pos_const) {
   at.layer = layer;
   at.pos = depth_model ? nullptr : c->at<int>(p.st_pos);
   at.pos_const = pos_const;
-  at.split = depth_model ? g.n_q : g.page_frames;
+  at.split = depth_model ? depth_indices(g) : g.page_frames;
   at.part = c->at<float>(depth_model ? p.part_d : p.part_t);
   at.max_splits = depth_model ? 1 : p.max_splits;  // number of key-range splits
   at.counters = c->at<int>(depth_model ? p.st_cnt_d : p.st_cnt_t);
@@ -540,13 +551,15 @@ ArgmaxArgs argmax_args(moshi_ctx* c, int slot) {
   } else {
     m.logits = c->at<float>(p.audio_logits) + (long long)(slot - 1) * g.codebook;
     m.n = g.codebook;
-    m.ld = g.n_q * g.codebook;
+    m.ld = depth_indices(g) * g.codebook;
   }
   m.slot = slot;
   // own slots are pad until their stream starts: the text after max(text_delay, 0)
-  // frames, the audio after max(-text_delay, 0), the acoustic codebooks delay later
+  // frames, the audio after max(-text_delay, 0), the acoustic codebooks delay
+  // later (the user's codebooks 9..16 like Moshi's 1..8)
   const int text_start = std::max(g.text_delay, 0), audio_start = std::max(-g.text_delay, 0);
-  m.start = slot == 0 ? text_start : (slot == 1 ? audio_start : audio_start + g.delay);
+  const int q = slot >= kSlots ? slot - kSlots + 1 : slot;
+  m.start = slot == 0 ? text_start : (q == 1 ? audio_start : audio_start + g.delay);
   m.pad_id = slot == 0 ? g.vocab_text : g.codebook;
   m.samp = c->at<int>(p.st_samp);
   if (slot == 0 && g.tts_max_tokens) {
@@ -556,10 +569,22 @@ ArgmaxArgs argmax_args(moshi_ctx* c, int slot) {
     m.tts_cap = g.tts_max_tokens;
   }
   m.pos = c->at<int>(p.st_pos);
-  m.out_tok = c->at<int>(p.st_out_tok);
-  m.cur_tok = c->at<int>(p.st_cur_tok);
-  m.force = c->at<int>(p.st_force);
-  m.has_force = c->at<int>(p.st_has_force);
+  if (slot < kSlots) {
+    m.out_tok = c->at<int>(p.st_out_tok);
+    m.cur_tok = c->at<int>(p.st_cur_tok);
+    m.force = c->at<int>(p.st_force);
+    m.has_force = c->at<int>(p.st_has_force);
+    m.stride = kSlots;
+    m.col = slot;
+  } else {
+    // the user's codebook slot - 9: given user codes act as forcing
+    m.out_tok = c->at<int>(p.st_user_own);
+    m.cur_tok = c->at<int>(p.st_user_cur);
+    m.force = c->at<int>(p.st_user);
+    m.has_force = c->at<int>(p.st_user_given);
+    m.stride = 8;
+    m.col = slot - kSlots;
+  }
   return m;
 }
 
@@ -628,7 +653,7 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   launch_gemv(ta, B, EPI_STORE, bf, s);
   launch_argmax(argmax_args(c, 0), B, s);
   if (depth) {
-    for (int j = 0; j < g.n_q; ++j) {
+    for (int j = 0; j < depth_indices(g); ++j) {
       const DepthW& w = p.dj[j];
       // u_j = W_in^j z + E_D^j[token of slot j]
       GemvArgs a{};
@@ -642,9 +667,15 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
       a.y = c->at<float>(p.hd);
       a.ldy = g.d_d;
       a.emb = c->ws + w.emb;
-      a.tok = c->at<int>(p.st_cur_tok);
-      a.tok_stride = kSlots;
-      a.tok_col = j;
+      if (j < kSlots) {
+        a.tok = c->at<int>(p.st_cur_tok);
+        a.tok_stride = kSlots;
+        a.tok_col = j;
+      } else {  // the user's codebook j - 9 (given or drawn at index j - 1)
+        a.tok = c->at<int>(p.st_user_cur);
+        a.tok_stride = 8;
+        a.tok_col = j - kSlots;
+      }
       a.tok_rows = (j == 0 ? g.vocab_text : g.codebook) + 1;
       stat_consume(c, a, B, false, nh);
       stat_produce(c, a, B, true);
@@ -674,7 +705,7 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
       hh.ldx = g.d_d;
       hh.gain = c->at<float>(w.out_norm);
       hh.y = c->at<float>(p.audio_logits) + (long long)j * g.codebook;
-      hh.ldy = g.n_q * g.codebook;
+      hh.ldy = depth_indices(g) * g.codebook;
       stat_consume(c, hh, B, true, nd);
       launch_gemv(hh, B, EPI_STORE, bf, s);
       launch_argmax(argmax_args(c, j + 1), B, s);
@@ -692,6 +723,7 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
   av.pad_audio = g.codebook;
   av.text_only = depth ? 0 : 1;
   av.out_tok = c->at<int>(p.st_out_tok);
+  av.user_cur = depth && depth_indices(g) == 16 ? c->at<int>(p.st_user_cur) : nullptr;
   launch_advance(av, B, s);
   HIPCHECK(hipGetLastError());
 }
@@ -1024,11 +1056,11 @@ int moshi_create(const moshi_config* cfg, void* hip_stream, void* workspace, siz
     HIPCHECK(hipEventCreateWithFlags(&c->ev_out, hipEventDisableTiming));
     const Plan& p = c->plan;
     const int mb = cfg->max_batch;
-    c->pinned_ints = mb * 8 + mb * kSlots + 1 + mb * kSlots + (size_t)mb * p.max_pages_conv + 2 + 64;
+    c->pinned_ints = mb * 8 + mb * kSlots + 1 + mb * kStreams + (size_t)mb * p.max_pages_conv + 2 + 64;
     HIPCHECK(hipHostMalloc((void**)&c->pinned, c->pinned_ints * 4 + 32 * 8, hipHostMallocDefault));
     c->pin_in = c->pinned;
     c->pin_out = c->pin_in + mb * 8 + mb * kSlots + 1;
-    c->pin_pt = c->pin_out + mb * kSlots;
+    c->pin_pt = c->pin_out + mb * kStreams;
     c->pin_one = c->pin_pt + (size_t)mb * p.max_pages_conv;
     c->pin_zero = c->pin_one + 1;
     c->pin_res = (double*)(c->pinned + ((c->pinned_ints + 1) & ~(size_t)1));
@@ -1040,7 +1072,8 @@ int moshi_create(const moshi_config* cfg, void* hip_stream, void* workspace, siz
     HIPCHECK(hipMemcpyAsync(c->ws + p.meta_row0, p.emb_row0, sizeof p.emb_row0, hipMemcpyHostToDevice, c->stream));
     HIPCHECK(hipMemcpyAsync(c->ws + p.meta_rows, p.emb_rows, sizeof p.emb_rows, hipMemcpyHostToDevice, c->stream));
     launch_rope_table(c->at<float>(p.rope_t), cfg->ctx_max, cfg->d_t / cfg->n_heads_t, cfg->rope_base, c->stream);
-    launch_rope_table(c->at<float>(p.rope_d), cfg->n_q, cfg->d_d / cfg->n_heads_d, cfg->rope_base, c->stream);
+    launch_rope_table(c->at<float>(p.rope_d), depth_indices(*cfg), cfg->d_d / cfg->n_heads_d, cfg->rope_base,
+                      c->stream);
     HIPCHECK(hipGetLastError());
     HIPCHECK(hipStreamSynchronize(c->stream));
     c->pos_h.assign(mb, 0);
@@ -1211,28 +1244,32 @@ int moshi_step(moshi_ctx* c, int32_t B, const int32_t* user, const int32_t* forc
     const Plan& p = c->plan;
     if (!c->ready) fail(MOSHI_ESTATE, "weights not loaded");
     if (B < 1 || B > g.max_batch) fail(MOSHI_EINVAL, "batch %d out of range 1..%d", B, g.max_batch);
-    if (!user || !out_tokens) fail(MOSHI_EINVAL, "user_codes and out_tokens are required");
+    const bool text_only = flags & MOSHI_STEP_TEXT_ONLY;
+    const bool sim = depth_indices(g) == 16;  // the depth also draws the user's codebooks
+    if (!out_tokens) fail(MOSHI_EINVAL, "out_tokens is required");
+    if (!user && (!sim || text_only))
+      fail(MOSHI_EINVAL, "user_codes are required unless a 16-index depth draws them");
     for (int b = 0; b < B; ++b)
       if (c->pos_h[b] + 1 > g.ctx_max) fail(MOSHI_ECONTEXT, "conversation %d is at ctx_max = %d", b, g.ctx_max);
     const bool dev = flags & MOSHI_DEVICE_PTRS;
     if (!dev) {
-      check_ids(user, (long long)B * 8, 8, 9, g);
+      if (user) check_ids(user, (long long)B * 8, 8, 9, g);
       if (force) check_ids(force, (long long)B * kSlots, kSlots, 0, g, -1);
     }
-    const bool text_only = flags & MOSHI_STEP_TEXT_ONLY;
     if (text_only && out_audio) fail(MOSHI_EINVAL, "MOSHI_STEP_TEXT_ONLY computes no audio logits");
     order_in(c);
     for (int b = 0; b < B; ++b) ensure_pages(c, b, c->pos_h[b] + 1);
     hipStream_t s = c->stream;
+    HIPCHECK(hipMemcpyAsync(c->ws + p.st_user_given, user ? c->pin_one : c->pin_zero, 4, hipMemcpyHostToDevice, s));
     if (dev) {
-      HIPCHECK(hipMemcpyAsync(c->ws + p.st_user, user, (size_t)B * 8 * 4, hipMemcpyDeviceToDevice, s));
+      if (user) HIPCHECK(hipMemcpyAsync(c->ws + p.st_user, user, (size_t)B * 8 * 4, hipMemcpyDeviceToDevice, s));
       if (force)
         HIPCHECK(hipMemcpyAsync(c->ws + p.st_force, force, (size_t)B * kSlots * 4, hipMemcpyDeviceToDevice, s));
       HIPCHECK(hipMemcpyAsync(c->ws + p.st_has_force, force ? c->pin_one : c->pin_zero, 4, hipMemcpyHostToDevice, s));
     } else {
       HIPCHECK(hipStreamSynchronize(s));  // the pinned input block may still be in use
       const int mb = g.max_batch;
-      memcpy(c->pin_in, user, (size_t)B * 8 * 4);
+      if (user) memcpy(c->pin_in, user, (size_t)B * 8 * 4);
       if (force) memcpy(c->pin_in + mb * 8, force, (size_t)B * kSlots * 4);
       c->pin_in[mb * 8 + mb * kSlots] = force ? 1 : 0;
       HIPCHECK(hipMemcpyAsync(c->ws + p.st_in, c->pin_in, (size_t)(mb * 8 + mb * kSlots + 1) * 4,
@@ -1240,18 +1277,22 @@ int moshi_step(moshi_ctx* c, int32_t B, const int32_t* user, const int32_t* forc
     }
     run_step(c, B, !text_only);
     const hipMemcpyKind k = dev ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost;
-    if (dev) {
-      HIPCHECK(hipMemcpyAsync(out_tokens, c->ws + p.st_out_tok, (size_t)B * kSlots * 4, k, s));
-    } else {
-      HIPCHECK(hipMemcpyAsync(c->pin_out, c->ws + p.st_out_tok, (size_t)B * kSlots * 4, k, s));
-    }
+    // own tokens: [B][9], or [B][17] with the user's draws (a text-only step
+    // reports the given user codes there)
+    const int row = sim ? kStreams : kSlots;
+    int* otk = dev ? out_tokens : c->pin_out;
+    HIPCHECK(hipMemcpy2DAsync(otk, (size_t)row * 4, c->ws + p.st_out_tok, kSlots * 4, kSlots * 4, B, k, s));
+    if (sim)
+      HIPCHECK(hipMemcpy2DAsync(otk + kSlots, (size_t)row * 4, c->ws + (text_only ? p.st_user : p.st_user_own), 8 * 4,
+                                8 * 4, B, k, s));
     if (out_text) HIPCHECK(hipMemcpyAsync(out_text, c->ws + p.text_logits, (size_t)B * g.vocab_text * 4, k, s));
     if (out_audio)
-      HIPCHECK(hipMemcpyAsync(out_audio, c->ws + p.audio_logits, (size_t)B * g.n_q * g.codebook * 4, k, s));
+      HIPCHECK(hipMemcpyAsync(out_audio, c->ws + p.audio_logits, (size_t)B * depth_indices(g) * g.codebook * 4, k,
+                              s));
     for (int b = 0; b < B; ++b) c->pos_h[b] += 1;
     if (!dev) {
       HIPCHECK(hipStreamSynchronize(s));
-      memcpy(out_tokens, c->pin_out, (size_t)B * kSlots * 4);
+      memcpy(out_tokens, c->pin_out, (size_t)B * row * 4);
     }
     order_out(c);
   });
@@ -1302,6 +1343,7 @@ int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B,
       }
     } else {
     HIPCHECK(hipMemcpyAsync(c->ws + p.st_has_force, c->pin_one, 4, hipMemcpyHostToDevice, s));
+    HIPCHECK(hipMemcpyAsync(c->ws + p.st_user_given, c->pin_one, 4, hipMemcpyHostToDevice, s));
     for (int st = 0; st < S; ++st) {
       HIPCHECK(hipMemcpy2DAsync(c->ws + p.st_user, 8 * 4, tok + (size_t)st * kStreams + kSlots,
                                 (size_t)S * kStreams * 4, 8 * 4, B, hipMemcpyDeviceToDevice, s));
@@ -1312,16 +1354,17 @@ int moshi_forward_teacher_forced(moshi_ctx* c, const int32_t* tokens, int32_t B,
         HIPCHECK(hipMemcpy2DAsync(text_logits + (size_t)st * g.vocab_text, (size_t)S * g.vocab_text * 4,
                                   c->ws + p.text_logits, (size_t)g.vocab_text * 4, (size_t)g.vocab_text * 4, B, k, s));
       if (audio_logits && depth) {
+        // Moshi's codebooks (a 16-index depth also wrote the user's after them)
         const size_t row = (size_t)g.n_q * g.codebook;
         HIPCHECK(hipMemcpy2DAsync(audio_logits + (size_t)st * row, (size_t)S * row * 4, c->ws + p.audio_logits,
-                                  row * 4, row * 4, B, k, s));
+                                  (size_t)depth_indices(g) * g.codebook * 4, row * 4, B, k, s));
       }
       if (loss) {
         CeRowsArgs ca{};
         ca.text_logits = c->at<float>(p.text_logits);
         ca.ld_text = g.vocab_text;
         ca.audio_logits = c->at<float>(p.audio_logits);
-        ca.ld_audio = (long long)g.n_q * g.codebook;
+        ca.ld_audio = (long long)depth_indices(g) * g.codebook;
         ca.targets = c->at<int>(p.st_force);
         ca.tgt_stride = kSlots;
         ca.vocab_text = g.vocab_text;

@@ -1847,8 +1847,9 @@ __global__ __launch_bounds__(HD) void k_attn_merge(AttnArgs a, int NS) {
 // (fp32 cache), one wave per (head, conversation), lane = head dimension
 // (hd <= 64). q, K and V are requested together, so the kernel waits on
 // memory once; softmax with max subtraction.
-constexpr int kDepthAttnKeys = 8;
+constexpr int kDepthAttnKeys = 16;
 
+template <int NK>
 __global__ __launch_bounds__(64) void k_attn_depth(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int hd = a.kv.hd;
@@ -1859,22 +1860,22 @@ __global__ __launch_bounds__(64) void k_attn_depth(AttnArgs a) {
   const long long kb = a.kv.offset(b, a.layer, 0, h, 0) + dim;
   const long long vb = a.kv.offset(b, a.layer, 1, h, 0) + dim;
   const float q = a.q[(long long)b * a.ldq + h * hd + dim] * a.scale;
-  float kk[kDepthAttnKeys], vv[kDepthAttnKeys];
+  float kk[NK], vv[NK];
 #pragma unroll
-  for (int t = 0; t < kDepthAttnKeys; ++t) {
+  for (int t = 0; t < NK; ++t) {
     const int tt = min(t, P - 1);
     kk[t] = kvb[kb + (long long)tt * hd];
     vv[t] = kvb[vb + (long long)tt * hd];
   }
-  float sc[kDepthAttnKeys], m = -INFINITY;
+  float sc[NK], m = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < kDepthAttnKeys; ++t) {
+  for (int t = 0; t < NK; ++t) {
     sc[t] = wave_sum(on ? q * kk[t] : 0.f);
     if (t < P) m = fmaxf(m, sc[t]);
   }
   float l = 0.f, o = 0.f;
 #pragma unroll
-  for (int t = 0; t < kDepthAttnKeys; ++t) {
+  for (int t = 0; t < NK; ++t) {
     if (t < P) {
       const float pr = expf(sc[t] - m);
       l += pr;
@@ -1887,7 +1888,10 @@ __global__ __launch_bounds__(64) void k_attn_depth(AttnArgs a) {
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s) {
   if (!a.kv.page_table && !a.pos && !kv_bf16 && a.pos_const < kDepthAttnKeys && a.pos_const < a.kv.pf &&
       hd <= 64 && a.kv.hd == hd) {
-    k_attn_depth<<<dim3(H, B), 64, 0, s>>>(a);
+    if (a.pos_const < 8)
+      k_attn_depth<8><<<dim3(H, B), 64, 0, s>>>(a);
+    else
+      k_attn_depth<16><<<dim3(H, B), 64, 0, s>>>(a);
     return;
   }
   if (a.kv.page_table && a.pos) {
@@ -2130,9 +2134,9 @@ __global__ __launch_bounds__(1024) void k_argmax(ArgmaxArgs a) {
     int* ctl = a.tts_ctl ? a.tts_ctl + b * kTtsCtl : nullptr;
     if (ctl && ctl[0] > 0) own = tts_choose(a, ctl, l, bv, own, sm);
     if (a.pos[b] < a.start) own = a.pad_id;
-    a.out_tok[b * kSlots + a.slot] = own;
-    const int f = *a.has_force ? a.force[b * kSlots + a.slot] : -1;
-    a.cur_tok[b * kSlots + a.slot] = f >= 0 ? f : own;
+    a.out_tok[b * a.stride + a.col] = own;
+    const int f = *a.has_force ? a.force[b * a.stride + a.col] : -1;
+    a.cur_tok[b * a.stride + a.col] = f >= 0 ? f : own;
   }
 }
 
@@ -2149,7 +2153,7 @@ __global__ void k_advance(AdvanceArgs a, int B) {
     const int hi = k == 0 ? a.pad_text : a.pad_audio;
     int v;
     if (k >= kSlots) {
-      v = a.user[b * 8 + (k - kSlots)];
+      v = a.user_cur ? a.user_cur[b * 8 + (k - kSlots)] : a.user[b * 8 + (k - kSlots)];
     } else {
       const int f = *a.has_force ? a.force[b * kSlots + k] : -1;
       if (f >= 0) v = f;

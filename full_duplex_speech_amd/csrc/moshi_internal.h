@@ -103,7 +103,8 @@ struct EmbedArgs {
 struct ArgmaxArgs {
   const float* logits;  // [B][ld]
   int n, ld;
-  int slot;
+  int slot;        // sub-stream 0..16 (counter of the sampling draw)
+  int stride, col; // row stride and column of out_tok, cur_tok and force
   int start;       // the slot is pad_id while pos[b] < start (its stream has not begun)
   int pad_id;
   const int* pos;
@@ -135,6 +136,7 @@ struct AdvanceArgs {
   int pad_text, pad_audio;
   int text_only;  // no depth ran: slots 1..8 are forced or pad, also written to out_tok
   int* out_tok;   // [B][9]
+  const int* user_cur;  // [B][8] user tokens of a 16-index depth (given or drawn), else null
 };
 
 struct CeRowsArgs {

@@ -83,6 +83,9 @@ typedef struct moshi_config {
                              every audio stream (streaming TTS, Fig. 9), 0 is the dialogue layout;
                              |text_delay| < ctx_max */
   int32_t tts_max_tokens; /* capacity of the per-conversation TTS text (moshi_tts_text); 0 = none */
+  int32_t n_depth;        /* depth indices: 0 or 8 = Moshi's codebooks; 16 = also the user's, after
+                             Moshi's in the same frame ([W] inference paragraph after Fig. 4: the
+                             user stream modelled as an output gives simulated dialogues) */
 } moshi_config;
 
 /* One weight tensor handed to moshi_init_weights: float32, C-order. Names and
@@ -159,6 +162,12 @@ int moshi_reset(moshi_ctx* ctx, int b);
  *       With a TTS text (moshi_tts_text) slot 0 is that control's choice.
  *   out_text_logits [batch][vocab_text], out_audio_logits [batch][8][codebook]:
  *       optional (NULL) float32 logits.
+ *   With n_depth = 16: out_tokens is [batch][17] (slots 9..16: the model's draws
+ *       of the user's codebooks), out_audio_logits [batch][16][codebook], and
+ *       user_codes may be NULL: the user's slots of the stored frame are then the
+ *       model's own draws (a simulated dialogue); given user codes drive the depth
+ *       inputs of indices 9..15 and the stored frame. A text-only step needs
+ *       user_codes and reports them in slots 9..16.
  *   flags: MOSHI_DEVICE_PTRS; MOSHI_STEP_TEXT_ONLY skips the Depth Transformer
  *       (streaming ASR discards the model's audio): slots 1..8 of out_tokens
  *       and of the stored frame are then the forced ids, or pad where force
@@ -205,7 +214,8 @@ int moshi_tts_text(moshi_ctx* ctx, int32_t conv, const int32_t* tokens, const in
 /* Teacher-forced pass over tokens [B][S][17] = V_1..V_S in model order
  * (inputs V_0..V_{S-1}, V_0 the pad frame) for conversations 0..B-1, which
  * must be at position 0. Outputs (each optional): text_logits [B][S][vocab_text],
- * audio_logits [B][S][8][codebook], loss. With MOSHI_TF_FILL_KV the
+ * audio_logits [B][S][8][codebook], loss (Moshi's 8 codebooks, also with
+ * n_depth = 16, whose user indices are a streaming feature). With MOSHI_TF_FILL_KV the
  * conversations continue streaming at frame S+1; otherwise they are reset. */
 int moshi_forward_teacher_forced(moshi_ctx* ctx, const int32_t* tokens, int32_t B, int32_t S,
                                  int32_t flags, float* text_logits, float* audio_logits,

@@ -11,6 +11,7 @@ from .moshi_oracle import (  # noqa: F401
     cross_entropy_loss,
     delay_codes,
     joint_sequence,
+    n_depth,
     rms_norm,
     rope,
     shift_stream,

@@ -85,6 +85,16 @@ def shift_stream(x: np.ndarray, n: int, pad: int) -> np.ndarray:
     return out
 
 
+def n_depth(cfg) -> int:
+    """Depth indices: Moshi's Q codebooks, or 2Q when the depth also predicts the
+    user's codebooks ([W] inference paragraph after Fig. 4: modelling the user
+    stream as an output lets the model generate both sides of a dialogue, used
+    for offline evaluation). READING: index j >= Q predicts sub-stream j + 1, the
+    user's codebook j - Q, with its own weights, after Moshi's Q in the same
+    frame-local causal chain."""
+    return 2 * cfg.n_q if int(getattr(cfg, "n_depth", cfg.n_q)) == 2 * cfg.n_q else cfg.n_q
+
+
 def stream_starts(cfg) -> Tuple[int, int]:
     """First step at which the text stream and the audio streams carry frame 1.
 
@@ -216,12 +226,13 @@ class Oracle:
         self.blocks = [_Block(weights, f"temporal.layers.{l}.", dt) for l in range(cfg.n_layers_t)]
         self.out_norm = g("temporal.out_norm")
         self.text_head = g("temporal.text_head")
-        self.d_in = [g(f"depth.{j}.in_proj") for j in range(cfg.n_q)]
-        self.d_emb = [g(f"depth.{j}.emb") for j in range(cfg.n_q)]
+        nd = n_depth(cfg)
+        self.d_in = [g(f"depth.{j}.in_proj") for j in range(nd)]
+        self.d_emb = [g(f"depth.{j}.emb") for j in range(nd)]
         self.d_blocks = [[_Block(weights, f"depth.{j}.layers.{l}.", dt) for l in range(cfg.n_layers_d)]
-                         for j in range(cfg.n_q)]
-        self.d_out_norm = [g(f"depth.{j}.out_norm") for j in range(cfg.n_q)]
-        self.d_head = [g(f"depth.{j}.head") for j in range(cfg.n_q)]
+                         for j in range(nd)]
+        self.d_out_norm = [g(f"depth.{j}.out_norm") for j in range(nd)]
+        self.d_head = [g(f"depth.{j}.head") for j in range(nd)]
 
     # -- frame layout ---------------------------------------------------------
     @property
@@ -346,9 +357,10 @@ class Oracle:
         z, text_logits = self.temporal(inp, 0, self.new_temporal_cache())
         audio = None
         if depth:
-            audio = np.empty((S, self.cfg.n_q, self.cfg.codebook), dtype=self.dt)
+            nd = n_depth(self.cfg)
+            audio = np.empty((S, nd, self.cfg.codebook), dtype=self.dt)
             cache = self.new_depth_cache(S)
-            for j in range(self.cfg.n_q):
+            for j in range(nd):
                 audio[:, j] = self.depth_position(j, z, V[:, j], cache)
         return text_logits, audio, z
 
@@ -385,7 +397,8 @@ class Session:
         exists: earlier own tokens are pad (``stream_starts``, ``delay_codes``)."""
         cfg = self.m.cfg
         t0, a0 = stream_starts(cfg)
-        return np.array([t0, a0] + [a0 + cfg.delay] * (cfg.n_q - 1))
+        audio = [a0] + [a0 + cfg.delay] * (cfg.n_q - 1)
+        return np.array([t0] + audio * (n_depth(cfg) // cfg.n_q))
 
     def step(self, user_codes: np.ndarray, force: Optional[np.ndarray] = None, text_only: bool = False,
              text_choice=None):
@@ -410,6 +423,12 @@ class Session:
         Returns (own tokens [n_q+1], text logits [vocab_text], audio logits
         [n_q, codebook]). Own tokens of a slot whose stream has not started are
         pad (``starts``).
+
+        With a 16-index depth (``n_depth``) the depth goes on to the user's
+        codebooks: own tokens and audio logits then have 2 n_q + 1 and 2 n_q
+        rows. ``user_codes`` may be None: the user's slots of the stored frame
+        are then the model's own draws (a simulated dialogue); given codes drive
+        the depth inputs and the stored frame instead.
         """
         m, cfg = self.m, self.m.cfg
         if self.pos + 1 > cfg.ctx_max:
@@ -417,7 +436,10 @@ class Session:
         st = self.starts()
         forced = (lambda k: force is not None and int(force[k]) >= 0)
         z, lt = m.temporal(self.prev[None, :], self.pos, self.cache)
-        own = np.empty(cfg.n_q + 1, dtype=np.int32)
+        nd = n_depth(cfg)
+        if user_codes is None and (nd == cfg.n_q or text_only):
+            raise ValueError("user codes are needed unless the depth predicts them")
+        own = np.empty(nd + 1, dtype=np.int32)
         pick_text = (lambda lg: self.pick(lg, 0))
         own[0] = int(text_choice(lt[0], pick_text)) if text_choice is not None else pick_text(lt[0])
         if self.pos < st[0]:
@@ -429,21 +451,26 @@ class Session:
             for j in range(cfg.n_q):
                 own[j + 1] = int(force[j + 1]) if forced(j + 1) else cfg.pad_audio
                 fed[j + 1] = own[j + 1]
+            for j in range(cfg.n_q, nd):
+                own[j + 1] = fed[j + 1] = user_codes[j - cfg.n_q]
         else:
-            audio = np.empty((cfg.n_q, cfg.codebook), dtype=m.dt)
+            audio = np.empty((nd, cfg.codebook), dtype=m.dt)
             dcache = m.new_depth_cache(1)
             tok = fed[0]
-            for j in range(cfg.n_q):
+            for j in range(nd):
                 audio[j] = m.depth_position(j, z, np.array([tok]), dcache)[0]
                 t = self.pick(audio[j], j + 1)
                 if self.pos < st[j + 1]:
                     t = cfg.pad_audio
                 own[j + 1] = t
-                fed[j + 1] = int(force[j + 1]) if forced(j + 1) else t
+                if j < cfg.n_q:
+                    fed[j + 1] = int(force[j + 1]) if forced(j + 1) else t
+                else:
+                    fed[j + 1] = t if user_codes is None else int(user_codes[j - cfg.n_q])
                 tok = fed[j + 1]
         frame = np.empty(cfg.n_streams, dtype=np.int32)
-        frame[:cfg.n_q + 1] = fed
-        frame[cfg.n_q + 1:] = user_codes
+        frame[:cfg.n_q + 1] = fed[:cfg.n_q + 1]
+        frame[cfg.n_q + 1:] = fed[cfg.n_q + 1:] if nd > cfg.n_q else user_codes
         self.prev = frame
         self.pos += 1
         return own, lt[0], audio

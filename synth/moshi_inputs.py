@@ -64,6 +64,7 @@ class MoshiConfig:
     tf_batch: int = 0
     tf_frames: int = 0
     mode: str = "dialogue"  # streaming workload: "dialogue", "asr" (audio forced, text only) or "tts"
+    n_depth: int = 8  # depth indices: 8 (Moshi's codebooks) or 16 (also the user's, simulated dialogues)
     temp_text: float = 0.0   # sampling temperatures of the own tokens (0 = greedy)
     temp_audio: float = 0.0
 
@@ -113,6 +114,18 @@ CONFIGS: Dict[str, MoshiConfig] = {
     "b1_7b_q8": MoshiConfig(
         name="b1_7b_q8", vocab_text=32000, dtype="q8", batch=1, prompt_frames=375,
         gen_frames=250, **_TEMPORAL_7B, **_DEPTH_7B),
+    # simulated dialogues: the depth also predicts the user's 8 codebooks
+    "tiny_sim": MoshiConfig(
+        name="tiny_sim", d_t=256, n_layers_t=2, n_heads_t=4, ffn_t=688, ctx_max=64,
+        d_d=128, n_layers_d=2, n_heads_d=4, ffn_d=352, vocab_text=1000, n_depth=16,
+        dtype="f32", batch=1, prompt_frames=0, gen_frames=40),
+    "mid_sim": MoshiConfig(
+        name="mid_sim", d_t=1024, n_layers_t=8, n_heads_t=16, ffn_t=2816, ctx_max=4096,
+        vocab_text=32000, n_depth=16, dtype="bf16", batch=1, prompt_frames=0, gen_frames=40,
+        **_DEPTH_7B),
+    "b1_7b_sim": MoshiConfig(
+        name="b1_7b_sim", vocab_text=32000, dtype="bf16", batch=1, prompt_frames=375,
+        gen_frames=250, n_depth=16, temp_text=0.7, temp_audio=0.8, **_TEMPORAL_7B, **_DEPTH_7B),
     # the batch-1 workload with temperature sampling (text 0.7, audio 0.8)
     "b1_7b_sampled": MoshiConfig(
         name="b1_7b_sampled", vocab_text=32000, dtype="bf16", batch=1, prompt_frames=375,
@@ -179,7 +192,7 @@ def weight_specs(cfg: MoshiConfig) -> List[Tuple[str, Tuple[int, ...], str]]:
             (p + "w_down", (d, F), "linear"),
         ]
     specs += [("temporal.out_norm", (d,), "ones"), ("temporal.text_head", (Vt, d), "linear")]
-    for j in range(cfg.n_q):
+    for j in range(cfg.n_depth):
         p = f"depth.{j}."
         rows = (Vt if j == 0 else NA) + 1
         specs += [(p + "in_proj", (dd, d), "linear"), (p + "emb", (rows, dd), "embed")]

@@ -180,3 +180,61 @@ def test_tts_text_control_bonus_only_below_target():
         TtsTextControl([[5]], pad_id=0, epad_id=1, target_pad_ratio=0.5, bonus=-1.0)
     with pytest.raises(ValueError):
         TtsTextControl([[5], []], pad_id=0, epad_id=1, target_pad_ratio=0.5, bonus=1.0)
+
+
+# ---------------------------------------------------------------- 16-index depth
+
+SIM = MICRO.replace(name="micro_sim", n_depth=16)
+
+
+def test_sixteen_index_depth_leaves_moshi_unchanged():
+    """The user's indices come after Moshi's in the depth chain: with the user's codes
+    given, text and Moshi's audio logits and tokens are bit-identical to the 8-index model
+    with the same weights."""
+    w16 = generate_weights(SIM, seed=0, threads=1)
+    w8 = {k: v for k, v in w16.items() if not k.startswith("depth.") or int(k.split(".")[1]) < 8}
+    m8, m16 = Oracle(MICRO, w8), Oracle(SIM, w16)
+    fr = raw_frames(MICRO, 0, 8)
+    V = joint_sequence(MICRO, fr["text"], fr["moshi"], fr["user"])
+    a, b = Session(m8), Session(m16)
+    for s in range(8):
+        o8, t8, a8 = a.step(V[s, 9:])
+        o16, t16, a16 = b.step(V[s, 9:])
+        assert o16.shape == (17,) and a16.shape == (16, MICRO.codebook)
+        np.testing.assert_array_equal(o8, o16[:9])
+        np.testing.assert_array_equal(t8, t16)
+        np.testing.assert_array_equal(a8, a16[:8])
+        np.testing.assert_array_equal(a.prev, b.prev)
+
+
+def test_simulated_dialogue_equals_teacher_forced():
+    """No user input: the user's slots are the model's own draws. The stream's 16 audio
+    logits match a teacher-forced pass over the realised sequence, and every own token is
+    its argmax once its stream has started (user slots follow the audio start rule)."""
+    w = generate_weights(SIM, seed=0, threads=1)
+    m = Oracle(SIM, w)
+    S = 10
+    sess = Session(m)
+    outs, realised = [], []
+    for s in range(S):
+        own, lt, la = sess.step(None)
+        outs.append((own, lt, la))
+        realised.append(own.copy())
+        np.testing.assert_array_equal(sess.prev, own)
+    _, la_tf, _ = m.forward_teacher_forced(np.array(realised))
+    for s, (own, lt, la) in enumerate(outs):
+        assert _rel(la, la_tf[s]) < 1e-12
+        for j in range(16):
+            acoustic = j % 8 != 0
+            pad = s < SIM.delay and acoustic
+            assert own[1 + j] == (SIM.pad_audio if pad else np.argmax(la_tf[s, j]))
+    with pytest.raises(ValueError):
+        Session(Oracle(MICRO, generate_weights(MICRO, seed=0, threads=1))).step(None)
+
+
+def test_sixteen_index_weights():
+    from synth import param_count, weight_specs
+    extra = param_count(SIM) - param_count(MICRO)
+    per_index = sum(int(np.prod(shape)) for name, shape, _ in weight_specs(SIM) if name.startswith("depth.8."))
+    assert extra == 8 * per_index
+    assert [n for n, _, _ in weight_specs(SIM) if n.endswith(".head")][-1] == "depth.15.head"
