@@ -5,7 +5,7 @@ prompt prefilled into the KV cache, then 250 greedy frames with new random user
 codes every frame. Prints one JSON line (frames/s, ms per frame, roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample).
 
-    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|mid_bf16|tiny]
+    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|b1_7b_sim|mimi_rvq|mid_bf16|tiny]
 """
 from __future__ import annotations
 
@@ -118,6 +118,64 @@ def cpu_baseline(cfg, weights, B, P, frames, prompts, users):
             "ms_per_frame": round(dt * 1000 / frames, 2)}
 
 
+def bench_rvq(args, torch, fds):
+    """Mimi's split RVQ: encode (512 -> 256 projection, semantic VQ + 7-level acoustic
+    RVQ over 2048 codewords) and decode (codeword sums, 256 -> 512) of 4 x 3750 latent
+    frames, seeded random latents, projections and codebooks."""
+    torch.cuda.set_device(0)
+    M, DZ, DQ, Q, N = 15000, 512, 256, 8, 2048
+    g = torch.Generator(device="cpu").manual_seed(0)
+    z = torch.randn(M, DZ, generator=g).cuda()
+    w_in = (torch.randn(DQ, DZ, generator=g) / DZ ** 0.5).cuda()
+    w_out = (torch.randn(DZ, DQ, generator=g) / DQ ** 0.5).cuda()
+    cb = (torch.randn(Q, N, DQ, generator=g) * 4 / DQ ** 0.5).cuda()
+    codes = torch.empty(M, Q, dtype=torch.int32, device="cuda")
+    zh = torch.empty(M, DZ, device="cuda")
+    work = torch.empty(fds.moshi_rvq_work_bytes(M, DQ, Q, N), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        fds.moshi_rvq_encode(z, M, DZ, w_in, DQ, cb, Q, N, codes, work, stream)
+        fds.moshi_rvq_decode(codes, M, cb, Q, N, DQ, w_out, DZ, zh, work, stream)
+
+    K = args.steps or 20
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / K
+    flops = 2.0 * M * DZ * DQ * 2 + Q * 2.0 * M * N * DQ  # projections + distances
+    ach = flops / dt / 1e12
+    cpu = None
+    if args.cpu_frames != 0:
+        from oracle.rvq import decode, encode
+        n = 200
+        zc, wi, wo, c = z[:n].cpu().numpy(), w_in.cpu().numpy(), w_out.cpu().numpy(), cb.cpu().numpy()
+        t1 = time.perf_counter()
+        cc, _ = encode(zc, wi, c)
+        decode(cc, c, wo)
+        ct = time.perf_counter() - t1
+        cpu = {"value": round(n / ct, 2), "unit": "frames/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"{n} latent frames encoded and decoded by the float64 NumPy oracle"}
+    out = {
+        "metric": "Mimi split-RVQ encode + decode latent frames/s", "value": round(M / dt, 1), "unit": "frames/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(dt * 1000, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded random latents, projections and codebooks)",
+        "config": {"workload": "Mimi split RVQ, 4 x 3750 latent frames, 512 -> 256, 8 codebooks x 2048",
+                   "config": "mimi_rvq", "frames": M},
+        "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(ach / 157.3, 4), "traffic": None,
+                     "kernel": "whole encode + decode (k_linear_f32, k_rvq_level x 8, k_rvq_sum)",
+                     "flops_per_step": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +195,9 @@ def main():
     import torch
     import full_duplex_speech_amd as fds
     from synth import config, generate_weights, param_count
+
+    if args.config == "mimi_rvq":
+        return bench_rvq(args, torch, fds)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -27,6 +27,9 @@ from .binding import (  # noqa: F401
     moshi_read_q8,
     moshi_tts_text,
     moshi_set_sampling,
+    moshi_rvq_work_bytes,
+    moshi_rvq_encode,
+    moshi_rvq_decode,
     moshi_reset,
     moshi_step,
     moshi_sync,

@@ -60,7 +60,7 @@ EXPORTS = (
     "moshi_workspace_bytes", "moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset",
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
     "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel", "moshi_read_q8",
-    "moshi_tts_text", "moshi_set_sampling",
+    "moshi_tts_text", "moshi_set_sampling", "moshi_rvq_work_bytes", "moshi_rvq_encode", "moshi_rvq_decode",
 )
 KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5, "tf_gate_up": 6,
            "tf_attn": 7}
@@ -95,12 +95,16 @@ def lib() -> ctypes.CDLL:
     L.moshi_read_q8.argtypes = [VP, ctypes.c_char_p, VP, VP, VP]
     L.moshi_tts_text.argtypes = [VP, I32, VP, VP, I32, I32, I32, ctypes.c_float, ctypes.c_float]
     L.moshi_set_sampling.argtypes = [VP, ctypes.c_float, ctypes.c_float, ctypes.c_uint64]
+    L.moshi_rvq_work_bytes.argtypes = [I32, I32, I32, I32]
+    L.moshi_rvq_work_bytes.restype = ctypes.c_size_t
+    L.moshi_rvq_encode.argtypes = [VP, I32, I32, VP, I32, VP, I32, I32, VP, VP, VP]
+    L.moshi_rvq_decode.argtypes = [VP, I32, VP, I32, I32, I32, VP, I32, VP, VP, VP]
     L.moshi_destroy.argtypes = [VP]
     L.moshi_destroy.restype = None
     for n in ("moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset", "moshi_step",
               "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
               "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8", "moshi_tts_text",
-              "moshi_set_sampling"):
+              "moshi_set_sampling", "moshi_rvq_encode", "moshi_rvq_decode"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -253,6 +257,24 @@ def moshi_tts_text(ctx, conv: int, words, pad_id: int, epad_id: int, target_pad_
 
 def moshi_set_sampling(ctx, temp_text: float, temp_audio: float, seed: int) -> None:
     _check(ctx, lib().moshi_set_sampling(ctx, temp_text, temp_audio, seed))
+
+
+def moshi_rvq_work_bytes(M: int, dq: int, Q: int, N: int) -> int:
+    return int(lib().moshi_rvq_work_bytes(M, dq, Q, N))
+
+
+def moshi_rvq_encode(z, M, dz, w_in, dq, codebooks, Q, N, codes, work, hip_stream=None) -> None:
+    rc = lib().moshi_rvq_encode(_ptr(z), M, dz, _ptr(w_in), dq, _ptr(codebooks), Q, N, _ptr(codes), _ptr(work),
+                                hip_stream)
+    if rc:
+        raise MoshiError(rc, "moshi_rvq_encode failed")
+
+
+def moshi_rvq_decode(codes, M, codebooks, Q, N, dq, w_out, dz, z_hat, work, hip_stream=None) -> None:
+    rc = lib().moshi_rvq_decode(_ptr(codes), M, _ptr(codebooks), Q, N, dq, _ptr(w_out), dz, _ptr(z_hat), _ptr(work),
+                                hip_stream)
+    if rc:
+        raise MoshiError(rc, "moshi_rvq_decode failed")
 
 
 def moshi_last_error(ctx) -> str:

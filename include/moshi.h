@@ -221,6 +221,24 @@ int moshi_forward_teacher_forced(moshi_ctx* ctx, const int32_t* tokens, int32_t 
                                  int32_t flags, float* text_logits, float* audio_logits,
                                  moshi_loss* loss);
 
+/* Split residual vector quantiser of the Mimi codec (walkthrough sections
+ * "量化率" and "使用分裂RVQ学习语义-声学token", Fig. 2; notes page 3a): the latent
+ * z [M][dz] (dz = 512) is projected by w_in [dq][dz] (dq = 256); codebook 0 is a
+ * plain VQ (semantic) and codebooks 1..Q-1 a residual VQ (acoustic), both applied
+ * to the projected latent; the nearest codeword minimises the squared Euclidean
+ * distance (float32, lowest index on ties). codebooks [Q][N][dq]; codes [M][Q].
+ * Decoding sums the Q chosen codewords and projects by w_out [dz][dq] into
+ * z_hat [M][dz]. All pointers are device pointers, float32 row-major; the calls
+ * enqueue on hip_stream (NULL: the default stream) and need a caller-owned
+ * device work buffer of moshi_rvq_work_bytes(M, dq, Q, N) bytes. dz and dq must
+ * be multiples of 64 with dq <= 256, 2 <= Q <= 32. MOSHI_EINVAL for bad sizes or
+ * null pointers (M = 0 does nothing), MOSHI_EHIP for a launch error. */
+size_t moshi_rvq_work_bytes(int32_t M, int32_t dq, int32_t Q, int32_t N);
+int moshi_rvq_encode(const float* z, int32_t M, int32_t dz, const float* w_in, int32_t dq, const float* codebooks,
+                     int32_t Q, int32_t N, int32_t* codes, void* work, void* hip_stream);
+int moshi_rvq_decode(const int32_t* codes, int32_t M, const float* codebooks, int32_t Q, int32_t N, int32_t dq,
+                     const float* w_out, int32_t dz, float* z_hat, void* work, void* hip_stream);
+
 /* Kernels that moshi_time_kernel can time. */
 #define MOSHI_KERNEL_QKV 0        /* RMSNorm + Wq|Wk|Wv + RoPE + KV append, one temporal layer */
 #define MOSHI_KERNEL_WO 1         /* output projection + residual, one temporal layer */
