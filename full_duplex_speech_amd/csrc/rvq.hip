@@ -6,8 +6,9 @@
 //
 // Kernels: a tiled float32 GEMM for the two projections, codeword norms, and one
 // nearest-codeword kernel per level. A block owns 32 latent rows (in LDS) and
-// walks the codebook in chunks of 32 codewords staged transposed in LDS; lane
-// l of a wave scores codeword l % 32 against 4 of the wave's 8 rows with
+// walks the codebook in chunks of 32 codewords staged in LDS as 16-byte groups
+// of 4 dimensions per codeword; lane l of a wave scores codeword l % 32 against
+// 4 of the wave's 8 rows (row groups read as broadcasts) with
 // distance ||c||^2 - 2 r.c (||r||^2 is common to a row), keeping the lowest
 // index on ties. An acoustic level then subtracts the chosen codewords from its
 // rows and writes the residual back.
@@ -85,14 +86,17 @@ __device__ __forceinline__ void keep_lower(float& bd, int& bi, float d, int i) {
 // acoustic residual; in and out may alias, a block owns its rows).
 __global__ __launch_bounds__(256) void k_rvq_level(const float* in, float* out, const float* C, const float* norms,
                                                    int N, int D, int M, int* codes, int Q, int q) {
-  __shared__ float rows[kRows][kMaxDim];
-  __shared__ float cs[kMaxDim][kChunk + 1];
+  __shared__ float4 rows4[kRows][kMaxDim / 4];
+  __shared__ float4 cs4[kMaxDim / 4][kChunk];  // [4 dims][codeword]: one 16-byte read per lane
   __shared__ int best_idx[kRows];
+  float* rows = (float*)rows4;  // [kRows][kMaxDim]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.x * kRows;
-  for (int i = tid; i < kRows * D; i += 256) {
-    const int r = i / D, k = i - r * D;
-    rows[r][k] = (m0 + r < M) ? in[(long long)(m0 + r) * D + k] : 0.f;
+  const int D4 = D / 4;
+  for (int i = tid; i < kRows * D4; i += 256) {
+    const int r = i / D4, k4 = i - r * D4;
+    rows4[r][k4] = (m0 + r < M) ? *(const float4*)(in + (long long)(m0 + r) * D + 4 * k4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   // lane: codeword lane % 32 of a chunk, rows wave*8 + (lane / 32) * 4 + 0..3
   const int cl = lane & 31, r0 = wave * 8 + (lane >> 5) * 4;
@@ -105,16 +109,23 @@ __global__ __launch_bounds__(256) void k_rvq_level(const float* in, float* out, 
   }
   for (int c0 = 0; c0 < N; c0 += kChunk) {
     __syncthreads();  // the previous chunk is consumed (and, first time, rows are in)
-    for (int i = tid; i < kChunk * D; i += 256) {
-      const int c = i / D, k = i - c * D;
-      cs[k][c] = (c0 + c < N) ? C[(long long)(c0 + c) * D + k] : 0.f;
+    for (int i = tid; i < kChunk * D4; i += 256) {
+      const int c = i / D4, k4 = i - c * D4;
+      cs4[k4][c] = (c0 + c < N) ? *(const float4*)(C + (long long)(c0 + c) * D + 4 * k4)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     float dot[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < D; ++k) {
-      const float cv = cs[k][cl];
+    for (int k4 = 0; k4 < D4; ++k4) {
+      const float4 cv = cs4[k4][cl];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dot[i] = fmaf(rows[r0 + i][k], cv, dot[i]);
+      for (int i = 0; i < 4; ++i) {
+        const float4 rv = rows4[r0 + i][k4];
+        dot[i] = fmaf(rv.x, cv.x, dot[i]);
+        dot[i] = fmaf(rv.y, cv.y, dot[i]);
+        dot[i] = fmaf(rv.z, cv.z, dot[i]);
+        dot[i] = fmaf(rv.w, cv.w, dot[i]);
+      }
     }
     const int c = c0 + cl;
     if (c < N) {
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(256) void k_rvq_level(const float* in, float* out, 
   for (int i = tid; i < kRows * D; i += 256) {
     const int r = i / D, k = i - r * D;
     const int b = best_idx[r] < N ? best_idx[r] : 0;  // NaN distances keep no index
-    if (m0 + r < M) out[(long long)(m0 + r) * D + k] = rows[r][k] - C[(long long)b * D + k];
+    if (m0 + r < M) out[(long long)(m0 + r) * D + k] = rows[r * kMaxDim + k] - C[(long long)b * D + k];
   }
 }
 
