@@ -15,3 +15,4 @@ from .moshi_inputs import (  # noqa: F401
     generate_weights,
     generate_weight,
 )
+from . import mimi_inputs  # noqa: F401,E402
