@@ -5,7 +5,7 @@ prompt prefilled into the KV cache, then 250 greedy frames with new random user
 codes every frame. Prints one JSON line (frames/s, ms per frame, roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample).
 
-    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|b1_7b_sim|mimi_rvq|mid_bf16|tiny]
+    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|b1_7b_sim|mimi_rvq|mimi_transformer|mid_bf16|tiny]
 """
 from __future__ import annotations
 
@@ -176,6 +176,70 @@ def bench_rvq(args, torch, fds):
     print(json.dumps(out), flush=True)
 
 
+def mimi_tf_flops(B, S, n_layers=8, d=512, f=2048, window=250):
+    """Algorithmic FLOP of the bottleneck Transformer: the four linear maps per layer and
+    attention over each query's min(t + 1, window) keys (QK^T and PV)."""
+    M = B * S
+    linear = 2.0 * M * (4 * d * d + 2 * d * f)
+    keys = sum(min(t + 1, window) for t in range(S)) * B
+    attn = 4.0 * keys * d
+    return n_layers * (linear + attn)
+
+
+def bench_mimi_transformer(args, torch, fds):
+    """Mimi's bottleneck Transformer (8 layers, width 512, 250-frame window) over 4 x 3750
+    latent frames, float32, seeded random weights and latents."""
+    from synth.mimi_inputs import latents, mimi_weights, pack
+    torch.cuda.set_device(0)
+    B, S, L, W = 4, 3750, 8, 250
+    wts = mimi_weights(L, seed=0, scale=0.1)
+    x0 = torch.from_numpy(latents(B, S, seed=0)).cuda()
+    x = x0.clone()
+    wd = torch.from_numpy(pack(wts, L)).cuda()
+    work = torch.empty(fds.moshi_mimi_transformer_work_bytes(B, S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        x.copy_(x0)
+        fds.moshi_mimi_transformer(x, B, S, wd, L, W, work, stream)
+
+    K = args.steps or 10
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / K
+    flops = mimi_tf_flops(B, S, L, window=W)
+    ach = flops / dt / 1e12
+    cpu = None
+    if args.cpu_frames != 0:
+        from oracle.mimi_transformer import forward
+        n = 250
+        xs = x0[0, :n].cpu().numpy()
+        t1 = time.perf_counter()
+        forward(xs, wts, L, 8, W)
+        ct = time.perf_counter() - t1
+        cpu = {"value": round(n / ct, 2), "unit": "frames/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"the first {n} frames of one sequence through the float64 NumPy oracle"}
+    out = {
+        "metric": "Mimi bottleneck Transformer latent frames/s", "value": round(B * S / dt, 1), "unit": "frames/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(dt * 1000, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded random latents and weights)",
+        "config": {"workload": "Mimi bottleneck Transformer, 8 layers x 512, 4 x 3750 frames, 250-frame window",
+                   "config": "mimi_transformer", "frames": B * S},
+        "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(ach / 157.3, 4), "traffic": None,
+                     "kernel": "whole pass (k_gemm_f32 x 4, k_window_attn, k_layer_norm x 2 per layer)",
+                     "flops_per_step": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +262,8 @@ def main():
 
     if args.config == "mimi_rvq":
         return bench_rvq(args, torch, fds)
+    if args.config == "mimi_transformer":
+        return bench_mimi_transformer(args, torch, fds)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

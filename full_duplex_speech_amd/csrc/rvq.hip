@@ -4,7 +4,7 @@
 // codebook 0) and a 7-level RVQ (acoustic codebooks 1..7) applied in parallel
 // to the projected latent, their codewords summed and projected back to 512.
 //
-// Kernels: a tiled float32 GEMM for the two projections, codeword norms, and one
+// Kernels: the tiled float32 GEMM of gemm_f32.h for the two projections, codeword norms, and one
 // nearest-codeword kernel per level. A block owns 32 latent rows (in LDS) and
 // walks the codebook in chunks of 32 codewords staged in LDS as 16-byte groups
 // of 4 dimensions per codeword; lane l of a wave scores codeword l % 32 against
@@ -19,50 +19,13 @@
 #include <stdexcept>
 
 #include "../../include/moshi.h"
+#include "gemm_f32.h"
 
 namespace {
 
 constexpr int kRows = 32;   // latent rows per block (4 waves x 8)
 constexpr int kChunk = 32;  // codewords per LDS chunk
 constexpr int kMaxDim = 256;
-
-// Y[M][N] = X[M][K] W[N][K]^T (+ nothing): 64 x 64 tile, 256 threads of 4 x 4
-__global__ __launch_bounds__(256) void k_linear_f32(const float* X, const float* W, float* Y, int M, int N, int K) {
-  __shared__ float As[16][64 + 1];
-  __shared__ float Bs[16][64 + 1];
-  const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int tm = (tid / 16) * 4, tn = (tid % 16) * 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int i = tid; i < 64 * 16; i += 256) {
-      const int r = i / 16, k = i % 16;
-      As[k][r] = (m0 + r < M) ? X[(long long)(m0 + r) * K + k0 + k] : 0.f;
-      Bs[k][r] = W[(long long)(n0 + r) * K + k0 + k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = As[k][tm + i];
-        b[i] = Bs[k][tn + i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (m0 + tm + i >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Y[(long long)(m0 + tm + i) * N + n0 + tn + j] = acc[i][j];
-  }
-}
 
 // ||c||^2 of every codeword, summed in dimension order
 __global__ void k_code_norms(const float* C, float* norms, long long n, int D) {
@@ -174,8 +137,7 @@ __global__ void k_rvq_sum(const int* codes, const float* C, int Q, int N, int D,
 }
 
 void linear(const float* X, const float* W, float* Y, int M, int N, int K, hipStream_t s) {
-  dim3 grid(N / 64, (M + 63) / 64);
-  k_linear_f32<<<grid, 256, 0, s>>>(X, W, Y, M, N, K);
+  moshi_f32::gemm_f32<moshi_f32::G_STORE>(X, W, Y, M, N, K, moshi_f32::GemmAux{}, s);
 }
 
 bool bad_shape(int32_t M, int32_t dz, int32_t dq, int32_t Q, int32_t N) {

@@ -239,6 +239,24 @@ int moshi_rvq_encode(const float* z, int32_t M, int32_t dz, const float* w_in, i
 int moshi_rvq_decode(const int32_t* codes, int32_t M, const float* codebooks, int32_t Q, int32_t N, int32_t dq,
                      const float* w_out, int32_t dz, float* z_hat, void* work, void* hip_stream);
 
+/* Bottleneck Transformer of the Mimi codec (walkthrough section "基于 Transformer
+ * 的瓶颈"; notes page 3a): n_layers pre-norm layers of width 512, 8 heads of 64,
+ * MLP width 2048, applied in place to x [B][S][512] (B sequences of S frames,
+ * positions from 0). Per layer:
+ *   x += scale1 * Wo Attn(LN1(x));  x += scale2 * W2 GELU(W1 LN2(x))
+ * LN: LayerNorm with gain and bias, eps 1e-5; GELU: x Phi(x) (erf); linear maps
+ * without bias; Attn: RoPE (base 10000, consecutive pairs) on q and k, causal,
+ * query t attending to keys t-window+1 .. t (the pages' 250 frames).
+ * weights: float32, layers back to back, each [ln1_g 512][ln1_b 512][Wq 512x512]
+ * [Wk][Wv][Wo][scale1 512][ln2_g 512][ln2_b 512][W1 2048x512][W2 512x2048]
+ * [scale2 512], matrices [out][in] row-major. Device pointers, float32; enqueued
+ * on hip_stream (NULL: default stream); work: a device buffer of
+ * moshi_mimi_transformer_work_bytes(B, S) bytes. MOSHI_EINVAL for bad sizes or
+ * null pointers (B*S = 0 does nothing), MOSHI_EHIP for a launch error. */
+size_t moshi_mimi_transformer_work_bytes(int32_t B, int32_t S);
+int moshi_mimi_transformer(float* x, int32_t B, int32_t S, const float* weights, int32_t n_layers, int32_t window,
+                           void* work, void* hip_stream);
+
 /* Kernels that moshi_time_kernel can time. */
 #define MOSHI_KERNEL_QKV 0        /* RMSNorm + Wq|Wk|Wv + RoPE + KV append, one temporal layer */
 #define MOSHI_KERNEL_WO 1         /* output projection + residual, one temporal layer */

@@ -24,10 +24,11 @@ READINGS (the pages list the ingredients, not the block):
 """
 from __future__ import annotations
 
-from math import erf, sqrt
+from math import sqrt
 from typing import Dict, List
 
 import numpy as np
+from scipy.special import erf
 
 D_MODEL, N_HEADS, D_MLP, N_LAYERS, WINDOW = 512, 8, 2048, 8, 250
 
@@ -38,12 +39,9 @@ def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray, eps: float = 1e-5) -
     return (x - mu) / np.sqrt(var + eps) * g + b
 
 
-_erf = np.vectorize(erf)
-
-
 def gelu(x: np.ndarray) -> np.ndarray:
     """x * Phi(x) = x * (1 + erf(x / sqrt 2)) / 2."""
-    return x * 0.5 * (1.0 + _erf(x / sqrt(2.0)))
+    return x * 0.5 * (1.0 + erf(x / sqrt(2.0)))
 
 
 def rope(x: np.ndarray, base: float = 10000.0) -> np.ndarray:
