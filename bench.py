@@ -5,7 +5,7 @@ prompt prefilled into the KV cache, then 250 greedy frames with new random user
 codes every frame. Prints one JSON line (frames/s, ms per frame, roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample).
 
-    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|b1_7b_sim|mimi_rvq|mimi_transformer|mid_bf16|tiny]
+    python bench.py [--steps K] [--warmup W] [--config b1_7b|b8_7b_5min|tf_7b|b1_7b_q8|b1_7b_asr|b1_7b_tts|b1_7b_sampled|b1_7b_sim|mimi_rvq|mimi_transformer|seanet|mid_bf16|tiny]
 """
 from __future__ import annotations
 
@@ -240,6 +240,84 @@ def bench_mimi_transformer(args, torch, fds):
     print(json.dumps(out), flush=True)
 
 
+def seanet_flops(B, S):
+    """Algorithmic FLOP of one SEANet encode + decode: 2 * C_in * C_out * k per output
+    sample of a convolution, per input sample of a transposed one."""
+    from synth.mimi_inputs import seanet_layers
+    enc, dec = seanet_layers()
+    total, T = 0.0, S * 1920
+    t = T
+    for name, kind, ci, co, k, st in enc:
+        t_out = t // st
+        total += 2.0 * ci * co * k * t_out
+        t = t_out
+    t = S
+    for name, kind, ci, co, k, st in dec:
+        if kind == "tconv":
+            total += 2.0 * ci * co * k * t
+            t *= st
+        else:
+            total += 2.0 * ci * co * k * t
+    return B * total
+
+
+def bench_seanet(args, torch, fds):
+    """Mimi's SEANet encoder + decoder over 4 x 3750 frames (4 x 5 minutes of 24 kHz
+    audio), float32, seeded weights and test signals."""
+    from synth.mimi_inputs import audio, pack_seanet, seanet_weights
+    torch.cuda.set_device(0)
+    B, S = 4, 3750
+    w = seanet_weights(seed=0)
+    a = torch.from_numpy(audio(B, S * 1920, seed=0)).cuda()
+    we = torch.from_numpy(pack_seanet(w, "enc")).cuda()
+    wd = torch.from_numpy(pack_seanet(w, "dec")).cuda()
+    lat = torch.empty((B, S, 512), device="cuda")
+    out = torch.empty((B, S * 1920), device="cuda")
+    work = torch.empty(fds.moshi_seanet_work_bytes(B, S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        fds.moshi_seanet_encode(a, B, S, we, lat, work, stream)
+        fds.moshi_seanet_decode(lat, B, S, wd, out, work, stream)
+
+    K = args.steps or 3
+    for _ in range(max(min(args.warmup, 2), 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / K
+    flops = seanet_flops(B, S)
+    ach = flops / dt / 1e12
+    cpu = None
+    if args.cpu_frames != 0:
+        from oracle.seanet import decode, encode
+        n = 4
+        x = audio(1, n * 1920, seed=0)[0]
+        t1 = time.perf_counter()
+        decode(encode(x, w), w)
+        ct = time.perf_counter() - t1
+        cpu = {"value": round(n / ct, 2), "unit": "frames/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"{n} frames ({n * 80} ms of audio) encoded and decoded by the float64 "
+                                           f"NumPy oracle"}
+    out_line = {
+        "metric": "Mimi SEANet encode + decode frames/s (80 ms of 24 kHz audio per frame)",
+        "value": round(B * S / dt, 1), "unit": "frames/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(dt * 1000, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded weights; sums of random sinusoids plus noise)",
+        "config": {"workload": "Mimi SEANet encoder + decoder, 4 x 3750 frames (4 x 5 min at 24 kHz)",
+                   "config": "seanet", "frames": B * S},
+        "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(ach / 157.3, 4), "traffic": None,
+                     "kernel": "whole encode + decode (k_conv_tiled, k_tconv_phase_weights)", "flops_per_step": flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +342,8 @@ def main():
         return bench_rvq(args, torch, fds)
     if args.config == "mimi_transformer":
         return bench_mimi_transformer(args, torch, fds)
+    if args.config == "seanet":
+        return bench_seanet(args, torch, fds)
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -61,7 +61,8 @@ EXPORTS = (
     "moshi_step", "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
     "moshi_undelay_codes", "moshi_last_error", "moshi_destroy", "moshi_time_kernel", "moshi_read_q8",
     "moshi_tts_text", "moshi_set_sampling", "moshi_rvq_work_bytes", "moshi_rvq_encode", "moshi_rvq_decode",
-    "moshi_mimi_transformer_work_bytes", "moshi_mimi_transformer",
+    "moshi_mimi_transformer_work_bytes", "moshi_mimi_transformer", "moshi_seanet_work_bytes", "moshi_seanet_encode",
+    "moshi_seanet_decode",
 )
 KERNELS = {"qkv": 0, "wo": 1, "ffn_gate_up": 2, "ffn_down": 3, "text_head": 4, "attn": 5, "tf_gate_up": 6,
            "tf_attn": 7}
@@ -103,13 +104,17 @@ def lib() -> ctypes.CDLL:
     L.moshi_mimi_transformer_work_bytes.argtypes = [I32, I32]
     L.moshi_mimi_transformer_work_bytes.restype = ctypes.c_size_t
     L.moshi_mimi_transformer.argtypes = [VP, I32, I32, VP, I32, I32, VP, VP]
+    L.moshi_seanet_work_bytes.argtypes = [I32, I32]
+    L.moshi_seanet_work_bytes.restype = ctypes.c_size_t
+    L.moshi_seanet_encode.argtypes = [VP, I32, I32, VP, VP, VP, VP]
+    L.moshi_seanet_decode.argtypes = [VP, I32, I32, VP, VP, VP, VP]
     L.moshi_destroy.argtypes = [VP]
     L.moshi_destroy.restype = None
     for n in ("moshi_check_config", "moshi_create", "moshi_init_weights", "moshi_reset", "moshi_step",
               "moshi_forward_teacher_forced", "moshi_sync", "moshi_position", "moshi_delay_codes",
               "moshi_undelay_codes", "moshi_time_kernel", "moshi_read_q8", "moshi_tts_text",
               "moshi_set_sampling", "moshi_rvq_encode", "moshi_rvq_decode",
-              "moshi_mimi_transformer"):
+              "moshi_mimi_transformer", "moshi_seanet_encode", "moshi_seanet_decode"):
         getattr(L, n).restype = ctypes.c_int
     _lib = L
     return L
@@ -290,6 +295,22 @@ def moshi_mimi_transformer(x, B, S, weights, n_layers, window, work, hip_stream=
     rc = lib().moshi_mimi_transformer(_ptr(x), B, S, _ptr(weights), n_layers, window, _ptr(work), hip_stream)
     if rc:
         raise MoshiError(rc, "moshi_mimi_transformer failed")
+
+
+def moshi_seanet_work_bytes(B: int, S: int) -> int:
+    return int(lib().moshi_seanet_work_bytes(B, S))
+
+
+def moshi_seanet_encode(audio, B, S, weights, latents, work, hip_stream=None) -> None:
+    rc = lib().moshi_seanet_encode(_ptr(audio), B, S, _ptr(weights), _ptr(latents), _ptr(work), hip_stream)
+    if rc:
+        raise MoshiError(rc, "moshi_seanet_encode failed")
+
+
+def moshi_seanet_decode(latents, B, S, weights, audio, work, hip_stream=None) -> None:
+    rc = lib().moshi_seanet_decode(_ptr(latents), B, S, _ptr(weights), _ptr(audio), _ptr(work), hip_stream)
+    if rc:
+        raise MoshiError(rc, "moshi_seanet_decode failed")
 
 
 def moshi_last_error(ctx) -> str:

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libmoshi.so")
-SOURCES = ["engine.hip", "kernels_decode.hip", "kernels_loss.hip", "kernels_tf.hip", "rvq.hip", "mimi.hip"]
+SOURCES = ["engine.hip", "kernels_decode.hip", "kernels_loss.hip", "kernels_tf.hip", "rvq.hip", "mimi.hip", "seanet.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

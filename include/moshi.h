@@ -257,6 +257,31 @@ size_t moshi_mimi_transformer_work_bytes(int32_t B, int32_t S);
 int moshi_mimi_transformer(float* x, int32_t B, int32_t S, const float* weights, int32_t n_layers, int32_t window,
                            void* work, void* hip_stream);
 
+/* SEANet encoder / decoder of the Mimi codec (walkthrough, Mimi's baseline
+ * architecture: causal residual convolution blocks with ELU, strides (4, 5, 6, 8)
+ * and a final stride-2 convolution, mirrored by transposed convolutions; notes
+ * page 3a). 24 kHz mono audio [B][S*1920] <-> latents [B][S][512] (12.5 frames/s).
+ * Architecture (the pages give the strides; the rest is this library's reading):
+ *   encoder: conv k7 1->64; per stride s in (4,5,6,8): residual unit
+ *     x + conv_k1(ELU(conv_k3(ELU(x)))) (C -> C/2 -> C), then ELU + conv k=2s
+ *     stride s (C -> 2C); ELU + conv k4 stride 2 (1024 -> 512).
+ *   decoder: transposed conv k4 stride 2 (512 -> 1024); per stride in (8,6,5,4):
+ *     ELU + transposed conv k=2s stride s (C -> C/2), residual unit; ELU + conv
+ *     k7 (64 -> 1).
+ * Causal: (k-1)+1-stride zeros on the left; transposed outputs past T*stride are
+ * dropped. No biases (weight normalisation folded into the weights).
+ * weights: float32, the encoder's (or the decoder's) convolutions back to back in
+ * the order above; conv [C_out][C_in][k], transposed [C_in][C_out][k]. Device
+ * pointers; enqueued on hip_stream (NULL: default); work: a device buffer of
+ * moshi_seanet_work_bytes(B, S) bytes (288 floats per sample and sequence).
+ * S * 1920 * 64 must fit in 31 bits. MOSHI_EINVAL for bad sizes or null pointers
+ * (B*S = 0 does nothing), MOSHI_EHIP for a launch error. */
+size_t moshi_seanet_work_bytes(int32_t B, int32_t S);
+int moshi_seanet_encode(const float* audio, int32_t B, int32_t S, const float* weights, float* latents, void* work,
+                        void* hip_stream);
+int moshi_seanet_decode(const float* latents, int32_t B, int32_t S, const float* weights, float* audio, void* work,
+                        void* hip_stream);
+
 /* Kernels that moshi_time_kernel can time. */
 #define MOSHI_KERNEL_QKV 0        /* RMSNorm + Wq|Wk|Wv + RoPE + KV append, one temporal layer */
 #define MOSHI_KERNEL_WO 1         /* output projection + residual, one temporal layer */
