@@ -25,11 +25,13 @@ struct GemmAux {
 
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K,
-                                                  GemmAux aux) {
+                                                  GemmAux aux, int rows_on_x) {
   __shared__ float4 As[16][16 + 1];  // [k][64 rows as 16 float4]
   __shared__ float4 Bs[16][16 + 1];
   const int tid = threadIdx.x;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  // column tiles on x (consecutive blocks share the input rows), unless there are
+  // more row tiles than grid y holds
+  const int m0 = (rows_on_x ? blockIdx.x : blockIdx.y) * 64, n0 = (rows_on_x ? blockIdx.y : blockIdx.x) * 64;
   const int ti = tid / 16, tj = tid % 16;  // rows 4ti.., cols 4tj..
   float acc[4][4] = {};
   const int lr = tid / 4, lk = (tid % 4) * 4;  // loader: row lr, columns lk..lk+3
@@ -92,8 +94,10 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* X, const float* W
 template <int EPI>
 inline void gemm_f32(const float* X, const float* W, float* Y, int M, int N, int K, const GemmAux& aux,
                      hipStream_t s) {
-  dim3 grid(N / 64, (M + 63) / 64);
-  k_gemm_f32<EPI><<<grid, 256, 0, s>>>(X, W, Y, M, N, K, aux);
+  const int mt = (M + 63) / 64, nt = N / 64;
+  const int rows_on_x = mt > 65535 ? 1 : 0;
+  const dim3 grid(rows_on_x ? mt : nt, rows_on_x ? nt : mt);
+  k_gemm_f32<EPI><<<grid, 256, 0, s>>>(X, W, Y, M, N, K, aux, rows_on_x);
 }
 
 }  // namespace moshi_f32

@@ -16,8 +16,6 @@
 
 #include <stdint.h>
 
-#include <stdexcept>
-
 #include "../../include/moshi.h"
 #include "gemm_f32.h"
 
