@@ -636,10 +636,14 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
     GemvArgs qa = qkv_args(c, w, l, false, 0);  // RMSNorm, Wqkv, RoPE, KV append
     stat_consume(c, qa, B, false, l == 0 ? (g.d_t + 255) / 256 : nh);
     launch_gemv(qa, B, EPI_QKV, bf, s);
-    launch_attn_decode(attn_args(c, l, false, 0), B, g.n_heads_t, hdt, bf, s);  // keys 0..pos
-    GemvArgs wa = wo_args(c, w, false);  // h += Wo attn
+    // keys 0..pos, then h += Wo attn (at B = 1 the split merge runs in Wo's prologue)
+    const AttnArgs at = attn_args(c, l, false, 0);
+    GemvArgs wa = wo_args(c, w, false);
     stat_produce(c, wa, B, false);
-    launch_gemv(wa, B, EPI_RESID, bf, s);
+    if (!launch_attn_wo(at, B, g.n_heads_t, hdt, bf, wa, bf, s)) {
+      launch_attn_decode(at, B, g.n_heads_t, hdt, bf, s);
+      launch_gemv(wa, B, EPI_RESID, bf, s);
+    }
     GemvArgs ga = gu_args(c, w, false);  // SiLU(Wg n) * Wu n
     stat_consume(c, ga, B, false, nh);
     launch_gemv(ga, B, EPI_SWIGLU, bf, s);
@@ -685,10 +689,15 @@ void enqueue_step(moshi_ctx* c, int B, bool depth) {
         GemvArgs dq = qkv_args(c, lw, l, true, j);
         stat_consume(c, dq, B, true, nd);
         launch_gemv(dq, B, EPI_QKV, bf, s);
-        launch_attn_decode(attn_args(c, l, true, j), B, g.n_heads_d, hdd, false, s);
+        // attention over this frame's positions 0..j, then h += Wo attn (at
+        // B = 1 the attention runs in Wo's prologue)
+        const AttnArgs dat = attn_args(c, l, true, j);
         GemvArgs dwo = wo_args(c, lw, true);
         stat_produce(c, dwo, B, true);
-        launch_gemv(dwo, B, EPI_RESID, bf, s);
+        if (!launch_attn_wo(dat, B, g.n_heads_d, hdd, false, dwo, bf, s)) {
+          launch_attn_decode(dat, B, g.n_heads_d, hdd, false, s);
+          launch_gemv(dwo, B, EPI_RESID, bf, s);
+        }
         GemvArgs dgu = gu_args(c, lw, true);
         stat_consume(c, dgu, B, true, nd);
         launch_gemv(dgu, B, EPI_SWIGLU, bf, s);

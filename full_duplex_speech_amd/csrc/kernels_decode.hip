@@ -428,6 +428,87 @@ __device__ __forceinline__ void pair_store(const GemvArgs& a, float* y, int row,
   }
 }
 
+// Where the prologue of a one-vector GEMV takes x from: XP_LOAD reads x (and
+// applies the RMSNorm gain), XP_ATTN computes the depth attention itself,
+// XP_MERGE merges the temporal attention's key-range partials.
+constexpr int XP_LOAD = 0, XP_ATTN = 1, XP_MERGE = 2;
+constexpr int kMergeMaxSplits = 8;
+
+// Causal attention of head h of one query over the keys 0..P-1 (P <= NK) of a
+// flat fp32 cache; lane = head dimension (hd <= 64), lanes past hd return 0.
+// q, K and V are requested together, so the wave waits on memory once;
+// softmax with max subtraction.
+template <int NK>
+__device__ __forceinline__ float depth_attn_lane(const float* q, const KvView& kv, int b, int layer, int h, int P,
+                                                 float scale, int lane) {
+  const int hd = kv.hd;
+  const bool on = lane < hd;
+  const int dim = on ? lane : 0;
+  const float* kvb = (const float*)kv.base;
+  const long long kb = kv.offset(b, layer, 0, h, 0) + dim;
+  const long long vb = kv.offset(b, layer, 1, h, 0) + dim;
+  const float qv = q[h * hd + dim] * scale;
+  float kk[NK], vv[NK];
+#pragma unroll
+  for (int t = 0; t < NK; ++t) {
+    const int tt = min(t, P - 1);
+    kk[t] = kvb[kb + (long long)tt * hd];
+    vv[t] = kvb[vb + (long long)tt * hd];
+  }
+  float sc[NK], m = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < NK; ++t) {
+    sc[t] = wave_sum(on ? qv * kk[t] : 0.f);
+    if (t < P) m = fmaxf(m, sc[t]);
+  }
+  float l = 0.f, o = 0.f;
+#pragma unroll
+  for (int t = 0; t < NK; ++t) {
+    if (t < P) {
+      const float pr = expf(sc[t] - m);
+      l += pr;
+      o = fmaf(pr, vv[t], o);
+    }
+  }
+  return on ? o / l : 0.f;
+}
+
+// x[k .. k+3] of the temporal attention output (k a multiple of 4, so the
+// four values lie in one head): that head's key-range partials merged in split
+// order, the arithmetic of the separate merge kernel; all partials are
+// requested together
+__device__ __forceinline__ float4 merge_x4(const GemvArgs& a, int k) {
+  const int hd = a.hd, NS = a.merge_ns;
+  const int h = k / hd, t = k - h * hd;
+  const float* part = a.merge_part + (long long)h * NS * (hd + 2);
+  float mx[kMergeMaxSplits], sm[kMergeMaxSplits], ov[kMergeMaxSplits][4];
+#pragma unroll
+  for (int i = 0; i < kMergeMaxSplits; ++i) {
+    if (i < NS) {
+      const float* pi = part + i * (hd + 2);
+      mx[i] = pi[hd];
+      sm[i] = pi[hd + 1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[i][e] = pi[t + e];
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeMaxSplits; ++i)
+    if (i < NS) M = fmaxf(M, mx[i]);
+  float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kMergeMaxSplits; ++i) {
+    if (i < NS) {
+      const float w = sm[i] > 0.f ? expf(mx[i] - M) : 0.f;
+      L = fmaf(w, sm[i], L);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(w, ov[i][e], o[e]);
+    }
+  }
+  return make_float4(o[0] / L, o[1] / L, o[2] / L, o[3] / L);
+}
+
 // Persistent variant of the streaming GEMV: a grid of about two blocks per CU;
 // every wave walks a sequence of units (row pair, K-group of LPG wave-wide
 // loads per row) assigned round-robin over all waves. The weight registers of
@@ -438,8 +519,9 @@ __device__ __forceinline__ void pair_store(const GemvArgs& a, float* y, int row,
 // zero-padded inputs or are never stored, and every operand the epilogue
 // needs (residual, embedding row, RoPE angle) is loaded before the refills,
 // so the compiler never has to drain the load queue.
-template <int NB, bool BF, int EPI, int LPG>
+template <int NB, bool BF, int EPI, int LPG, int XP = XP_LOAD>
 __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) {
+  static_assert(XP == XP_LOAD || (XP == XP_MERGE && NB == 1), "the merge prologue takes one input vector");
   constexpr int EPL = WLoad<BF>::EPL, SPAN = 64 * EPL, GROUP = SPAN * LPG;
   constexpr int ESZ = BF ? 2 : 4;
   extern __shared__ float4 xs4[];  // [NB][KP], zero past K
@@ -492,7 +574,9 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
   for (int i = tid * 4; i < NB * KP; i += 64 * kStreamWaves * 4) {
     const int b = i / KP, k = i - b * KP;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < K) {
+    if constexpr (XP == XP_MERGE) {
+      if (k < K) v = merge_x4(a, k);
+    } else if (k < K) {
       v = *(const float4*)(a.x + (long long)b * a.ldx + k);
       if (a.gain) {
         const float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -639,7 +723,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
 // CUs share the matrix. All weight loads are issued before the RMSNorm
 // prologue; spans past K read clamped addresses against zero-padded inputs.
 // The SK partial sums meet in LDS and are added in wave order.
-template <bool BF, int EPI, int SPW>
+template <bool BF, int EPI, int SPW, int XP = XP_LOAD>
 __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, int SK) {
   constexpr int EPL = WLoad<BF>::EPL, SPAN = 64 * EPL, ESZ = BF ? 2 : 4;
   extern __shared__ float4 xs4[];  // [SK * SPW * SPAN], zero past K
@@ -687,9 +771,22 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, i
   // one read of x: LDS gets gain * x (zero-padded) and the same pass sums x^2;
   // the RMSNorm factor scales the dot products in the epilogue
   float rs = 0.f;
-  for (int k = tid * 4; k < KPAD; k += 64 * kStreamWaves * 4) {
+  if constexpr (XP == XP_ATTN) {
+    // x = the depth attention output: wave w takes heads w, w + 8, ...
+    for (int k = K + tid * 4; k < KPAD; k += 64 * kStreamWaves * 4) xs4[k >> 2] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float* xs = (float*)xs4;
+    const int P = a.pos_const + 1;
+    for (int h = wave; h * a.hd < K; h += kStreamWaves) {
+      const float o = P <= 8 ? depth_attn_lane<8>(a.attn_q, a.kv, 0, a.layer, h, P, a.attn_scale, lane)
+                             : depth_attn_lane<16>(a.attn_q, a.kv, 0, a.layer, h, P, a.attn_scale, lane);
+      if (lane < a.hd) xs[h * a.hd + lane] = o;
+    }
+  }
+  for (int k = tid * 4; XP != XP_ATTN && k < KPAD; k += 64 * kStreamWaves * 4) {
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (k < K) {
+    if (XP == XP_MERGE && k < K) {
+      v = merge_x4(a, k);
+    } else if (k < K) {
       v = *(const float4*)(a.x + k);
       if (a.gain) {
         rs += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
@@ -1397,9 +1494,15 @@ static int device_cus() {
 
 // one input vector and fewer row pairs than kSplitWaves: split K over the
 // waves of a block (k_gemv_splitk); false when the shape does not qualify
-constexpr int kSplitWaves = 2048;
+#ifndef MOSHI_LPG_MAX
+#define MOSHI_LPG_MAX 8
+#endif
+#ifndef MOSHI_SPLIT_WAVES
+#define MOSHI_SPLIT_WAVES 2048
+#endif
+constexpr int kSplitWaves = MOSHI_SPLIT_WAVES;
 
-template <bool BF, int SPW>
+template <bool BF, int SPW, int XP = XP_LOAD>
 static void splitk_launch(const GemvArgs& a, int epi, int SK, hipStream_t s) {
   constexpr int SPAN = 64 * WLoad<BF>::EPL;
   const int RG = kStreamWaves / SK;
@@ -1407,6 +1510,10 @@ static void splitk_launch(const GemvArgs& a, int epi, int SK, hipStream_t s) {
   dim3 grid((npairs + RG - 1) / RG);
   const size_t lds = (size_t)SK * SPW * SPAN * sizeof(float);
   const int T = 64 * kStreamWaves;
+  if constexpr (XP != XP_LOAD) {
+    k_gemv_splitk<BF, EPI_RESID, SPW, XP><<<grid, T, lds, s>>>(a, SK);
+    return;
+  }
   switch (epi) {
     case EPI_STORE: k_gemv_splitk<BF, EPI_STORE, SPW><<<grid, T, lds, s>>>(a, SK); break;
     case EPI_RESID: k_gemv_splitk<BF, EPI_RESID, SPW><<<grid, T, lds, s>>>(a, SK); break;
@@ -1416,7 +1523,9 @@ static void splitk_launch(const GemvArgs& a, int epi, int SK, hipStream_t s) {
   }
 }
 
-static bool gemv_splitk(const GemvArgs& a, int epi, bool bf16, hipStream_t s) {
+// split factor SK and spans per wave of the split-K route, or false when the
+// shape does not take it
+static bool splitk_plan(const GemvArgs& a, bool bf16, int* SKo, int* spwo) {
   const int target = kSplitWaves;
   const int span = bf16 ? 512 : 256;
   const int npairs = (a.N + 1) / 2;
@@ -1428,17 +1537,46 @@ static bool gemv_splitk(const GemvArgs& a, int epi, bool bf16, hipStream_t s) {
   const int need = (nspans + SK - 1) / SK;
   const int spw = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
   if (need > 8 || (size_t)SK * spw * span * sizeof(float) > 65536) return false;
+  *SKo = SK;
+  *spwo = spw;
+  return true;
+}
+
+template <int XP>
+static bool gemv_splitk_xp(const GemvArgs& a, int epi, bool bf16, hipStream_t s) {
+  int SK, spw;
+  if (!splitk_plan(a, bf16, &SK, &spw)) return false;
   if (bf16) {
-    if (spw == 1) splitk_launch<true, 1>(a, epi, SK, s);
-    else if (spw == 2) splitk_launch<true, 2>(a, epi, SK, s);
-    else if (spw == 4) splitk_launch<true, 4>(a, epi, SK, s);
-    else splitk_launch<true, 8>(a, epi, SK, s);
+    if (spw == 1) splitk_launch<true, 1, XP>(a, epi, SK, s);
+    else if (spw == 2) splitk_launch<true, 2, XP>(a, epi, SK, s);
+    else if (spw == 4) splitk_launch<true, 4, XP>(a, epi, SK, s);
+    else splitk_launch<true, 8, XP>(a, epi, SK, s);
   } else {
-    if (spw == 1) splitk_launch<false, 1>(a, epi, SK, s);
-    else if (spw == 2) splitk_launch<false, 2>(a, epi, SK, s);
-    else if (spw == 4) splitk_launch<false, 4>(a, epi, SK, s);
-    else splitk_launch<false, 8>(a, epi, SK, s);
+    if (spw == 1) splitk_launch<false, 1, XP>(a, epi, SK, s);
+    else if (spw == 2) splitk_launch<false, 2, XP>(a, epi, SK, s);
+    else if (spw == 4) splitk_launch<false, 4, XP>(a, epi, SK, s);
+    else splitk_launch<false, 8, XP>(a, epi, SK, s);
   }
+  return true;
+}
+
+static bool gemv_splitk(const GemvArgs& a, int epi, bool bf16, hipStream_t s) {
+  return gemv_splitk_xp<XP_LOAD>(a, epi, bf16, s);
+}
+
+// loads per group and padded K of the one-vector persistent route (NB input
+// vectors), or false when x does not fit in LDS
+template <bool BF>
+static bool persist_plan(const GemvArgs& a, int NB, int* lpgo, size_t* ldso) {
+  if ((size_t)NB * a.K * sizeof(float) > 65536) return false;
+  constexpr int EPL = WLoad<BF>::EPL;
+  const int slots = (a.K + 64 * EPL - 1) / (64 * EPL);
+  const int lpg = std::min(slots <= 2 ? 2 : (slots <= 4 ? 4 : 8), MOSHI_LPG_MAX);
+  const int KP = ((a.K + 64 * EPL * lpg - 1) / (64 * EPL * lpg)) * 64 * EPL * lpg;
+  const size_t lds_p = (size_t)NB * KP * sizeof(float);
+  if (lds_p > 65536) return false;
+  *lpgo = lpg;
+  *ldso = lds_p;
   return true;
 }
 
@@ -1447,31 +1585,24 @@ static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s)
   if constexpr (NB == 1) {
     if (gemv_splitk(a, epi, BF, s)) return;
   }
-  if ((size_t)NB * a.K * sizeof(float) <= 65536) {
+  int lpg;
+  size_t lds_p;
+  if (persist_plan<BF>(a, NB, &lpg, &lds_p)) {
     const int need = ((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
     dim3 grid(std::min(need, 2 * device_cus()));
-    const size_t lds = (size_t)NB * a.K * sizeof(float);
     const int T = 64 * kStreamWaves;
-    constexpr int EPL = WLoad<BF>::EPL;
-    const int slots = (a.K + 64 * EPL - 1) / (64 * EPL);
-    const int lpg = slots <= 2 ? 2 : (slots <= 4 ? 4 : 8);
-    const int KP = ((a.K + 64 * EPL * lpg - 1) / (64 * EPL * lpg)) * 64 * EPL * lpg;
-    const size_t lds_p = (size_t)NB * KP * sizeof(float);
 #define MOSHI_GP(E, L) k_gemv_persist<NB, BF, E, L><<<grid, T, lds_p, s>>>(a)
 #define MOSHI_GPL(E) (lpg == 2 ? MOSHI_GP(E, 2) : (lpg == 4 ? MOSHI_GP(E, 4) : MOSHI_GP(E, 8)))
-    if (lds_p <= 65536) {
-      switch (epi) {
-        case EPI_STORE: MOSHI_GPL(EPI_STORE); break;
-        case EPI_RESID: MOSHI_GPL(EPI_RESID); break;
-        case EPI_EMB: MOSHI_GPL(EPI_EMB); break;
-        case EPI_SWIGLU: MOSHI_GPL(EPI_SWIGLU); break;
-        case EPI_QKV: MOSHI_GPL(EPI_QKV); break;
-      }
-      return;
+    switch (epi) {
+      case EPI_STORE: MOSHI_GPL(EPI_STORE); break;
+      case EPI_RESID: MOSHI_GPL(EPI_RESID); break;
+      case EPI_EMB: MOSHI_GPL(EPI_EMB); break;
+      case EPI_SWIGLU: MOSHI_GPL(EPI_SWIGLU); break;
+      case EPI_QKV: MOSHI_GPL(EPI_QKV); break;
     }
+    return;
 #undef MOSHI_GPL
 #undef MOSHI_GP
-    (void)lds;
   }
   dim3 grid((a.N + kGemvRows - 1) / kGemvRows);
   size_t lds = (size_t)NB * (size_t)KC * sizeof(float);
@@ -1852,42 +1983,48 @@ constexpr int kDepthAttnKeys = 16;
 template <int NK>
 __global__ __launch_bounds__(64) void k_attn_depth(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int hd = a.kv.hd;
-  const bool on = lane < hd;
-  const int dim = on ? lane : 0;
   const int P = (a.pos ? a.pos[b] : a.pos_const) + 1;
-  const float* kvb = (const float*)a.kv.base;
-  const long long kb = a.kv.offset(b, a.layer, 0, h, 0) + dim;
-  const long long vb = a.kv.offset(b, a.layer, 1, h, 0) + dim;
-  const float q = a.q[(long long)b * a.ldq + h * hd + dim] * a.scale;
-  float kk[NK], vv[NK];
-#pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    const int tt = min(t, P - 1);
-    kk[t] = kvb[kb + (long long)tt * hd];
-    vv[t] = kvb[vb + (long long)tt * hd];
+  const float o = depth_attn_lane<NK>(a.q + (long long)b * a.ldq, a.kv, b, a.layer, h, P, a.scale, lane);
+  if (lane < a.kv.hd) a.out[(long long)b * a.ldo + h * a.kv.hd + lane] = o;
+}
+
+static bool depth_attn_ok(const AttnArgs& a, int hd, bool kv_bf16) {
+  return !a.kv.page_table && !a.pos && !kv_bf16 && a.pos_const < kDepthAttnKeys && a.pos_const < a.kv.pf &&
+         hd <= 64 && a.kv.hd == hd;
+}
+
+// temporal cache: about half a block per CU over (split, head, conversation);
+// at batch 1 and ~500 keys, 4 splits of 32 heads beat 8 (4.11 vs 4.16 ms per
+// frame) and 16-wave blocks without splits are no better
+static int attn_range_splits(const AttnArgs& a, int B, int H) {
+  return std::max(1, std::min(std::min(a.max_splits, kMaxAttnSplits), 128 / (B * H)));
+}
+
+// key-range attention over the paged cache; the splits are merged by
+// k_attn_merge unless `merge` is false (the consumer merges them)
+static void launch_attn_range(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, int NS, bool merge,
+                              hipStream_t s) {
+  dim3 grid(NS, H, B);
+  const int T = 64 * kAttnWaves;
+#define MOSHI_AR(KB, HDV)                                                  \
+  do {                                                                     \
+    k_attn_range<KB, HDV><<<grid, T, 0, s>>>(a);                           \
+    if (NS > 1 && merge) k_attn_merge<HDV><<<dim3(H, B), HDV, 0, s>>>(a, NS); \
+  } while (0)
+  if (kv_bf16) {
+    if (hd == 32) MOSHI_AR(true, 32);
+    else if (hd == 64) MOSHI_AR(true, 64);
+    else MOSHI_AR(true, 128);
+  } else {
+    if (hd == 32) MOSHI_AR(false, 32);
+    else if (hd == 64) MOSHI_AR(false, 64);
+    else MOSHI_AR(false, 128);
   }
-  float sc[NK], m = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    sc[t] = wave_sum(on ? q * kk[t] : 0.f);
-    if (t < P) m = fmaxf(m, sc[t]);
-  }
-  float l = 0.f, o = 0.f;
-#pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    if (t < P) {
-      const float pr = expf(sc[t] - m);
-      l += pr;
-      o = fmaf(pr, vv[t], o);
-    }
-  }
-  if (on) a.out[(long long)b * a.ldo + h * hd + dim] = o / l;
+#undef MOSHI_AR
 }
 
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s) {
-  if (!a.kv.page_table && !a.pos && !kv_bf16 && a.pos_const < kDepthAttnKeys && a.pos_const < a.kv.pf &&
-      hd <= 64 && a.kv.hd == hd) {
+  if (depth_attn_ok(a, hd, kv_bf16)) {
     if (a.pos_const < 8)
       k_attn_depth<8><<<dim3(H, B), 64, 0, s>>>(a);
     else
@@ -1895,27 +2032,7 @@ void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, h
     return;
   }
   if (a.kv.page_table && a.pos) {
-    // temporal cache: about half a block per CU over (split, head, conversation);
-    // at batch 1 and ~500 keys, 4 splits of 32 heads beat 8 (4.11 vs 4.16 ms per
-    // frame) and 16-wave blocks without splits are no better
-    const int NS = std::max(1, std::min(std::min(a.max_splits, kMaxAttnSplits), 128 / (B * H)));
-    dim3 grid(NS, H, B);
-    const int T = 64 * kAttnWaves;
-#define MOSHI_AR(KB, HDV)                                                  \
-  do {                                                                     \
-    k_attn_range<KB, HDV><<<grid, T, 0, s>>>(a);                           \
-    if (NS > 1) k_attn_merge<HDV><<<dim3(H, B), HDV, 0, s>>>(a, NS);       \
-  } while (0)
-    if (kv_bf16) {
-      if (hd == 32) MOSHI_AR(true, 32);
-      else if (hd == 64) MOSHI_AR(true, 64);
-      else MOSHI_AR(true, 128);
-    } else {
-      if (hd == 32) MOSHI_AR(false, 32);
-      else if (hd == 64) MOSHI_AR(false, 64);
-      else MOSHI_AR(false, 128);
-    }
-#undef MOSHI_AR
+    launch_attn_range(a, B, H, hd, kv_bf16, attn_range_splits(a, B, H), true, s);
     return;
   }
   const int NS = a.max_splits;
@@ -1935,6 +2052,49 @@ void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, h
     else MOSHI_ATTN(false, 128);
   }
 #undef MOSHI_ATTN
+}
+
+bool launch_attn_wo(const AttnArgs& at, int B, int H, int hd, bool kv_bf16, GemvArgs wo, bool bf16, hipStream_t s) {
+  if (B != 1 || wo.Wq8p || wo.stat_in || wo.stat_out || wo.gain || wo.K != H * hd || hd % 4 != 0) return false;
+  int SK, spw, lpg;
+  size_t lds;
+  if (depth_attn_ok(at, hd, kv_bf16)) {
+    // the whole depth attention in the split-K prologue
+    if (!splitk_plan(wo, bf16, &SK, &spw)) return false;
+    wo.attn_q = at.q;
+    wo.attn_scale = at.scale;
+    wo.kv = at.kv;
+    wo.layer = at.layer;
+    wo.pos_const = at.pos_const;
+    wo.hd = hd;
+    return gemv_splitk_xp<XP_ATTN>(wo, EPI_RESID, bf16, s);
+  }
+  if (!at.kv.page_table || !at.pos || (hd != 32 && hd != 64 && hd != 128)) return false;
+  const int NS = attn_range_splits(at, B, H);
+  if (NS < 2 || NS > kMergeMaxSplits) return false;
+  wo.merge_part = at.part;
+  wo.merge_ns = NS;
+  wo.hd = hd;
+  const bool sk = splitk_plan(wo, bf16, &SK, &spw);
+  const bool ps = bf16 ? persist_plan<true>(wo, 1, &lpg, &lds) : persist_plan<false>(wo, 1, &lpg, &lds);
+  if (!sk && !ps) return false;
+  launch_attn_range(at, B, H, hd, kv_bf16, NS, false, s);
+  if (sk) return gemv_splitk_xp<XP_MERGE>(wo, EPI_RESID, bf16, s);
+  const int need = ((wo.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
+  dim3 grid(std::min(need, 2 * device_cus()));
+  const int T = 64 * kStreamWaves;
+#define MOSHI_GM(BFV, L) k_gemv_persist<1, BFV, EPI_RESID, L, XP_MERGE><<<grid, T, lds, s>>>(wo)
+  if (bf16) {
+    if (lpg == 2) MOSHI_GM(true, 2);
+    else if (lpg == 4) MOSHI_GM(true, 4);
+    else MOSHI_GM(true, 8);
+  } else {
+    if (lpg == 2) MOSHI_GM(false, 2);
+    else if (lpg == 4) MOSHI_GM(false, 4);
+    else MOSHI_GM(false, 8);
+  }
+#undef MOSHI_GM
+  return true;
 }
 
 // ---------------------------------------------------------------------------

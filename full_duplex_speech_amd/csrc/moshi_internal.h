@@ -70,6 +70,17 @@ struct GemvArgs {
   const int* tok;
   int tok_stride, tok_col;
   int tok_rows;  // rows of emb (ids are clamped into range)
+  // Output projection of one input vector (B = 1) with the attention finished
+  // in the GEMV prologue, so that x is not read:
+  //  - attn_q set: x = causal attention of the query heads attn_q (head h at
+  //    h * hd) over keys 0..pos_const of the flat fp32 cache kv at `layer`,
+  //    scores scaled by attn_scale (the depth model's at most 16 keys);
+  //  - merge_part set: x = the merge of merge_ns key-range partials per head,
+  //    [H][merge_ns][hd + 2] = (unnormalised o, running max, running sum)
+  const float* attn_q;
+  float attn_scale;
+  const float* merge_part;
+  int merge_ns;
 };
 
 struct AttnArgs {
@@ -211,6 +222,11 @@ struct TfCeArgs {
 // launchers (kernels_decode.hip)
 void launch_gemv(const GemvArgs& a, int B, int epi, bool bf16, hipStream_t s);
 void launch_attn_decode(const AttnArgs& a, int B, int H, int hd, bool kv_bf16, hipStream_t s);
+// Attention followed by the output projection wo (EPI_RESID) at B = 1, with
+// the attention's last step (the depth model's whole attention, or the merge
+// of the temporal key-range splits) done in the projection's prologue. Returns
+// false, launching nothing, when the shapes do not take the fused route.
+bool launch_attn_wo(const AttnArgs& at, int B, int H, int hd, bool kv_bf16, GemvArgs wo, bool bf16, hipStream_t s);
 void launch_embed(const EmbedArgs& a, int B, bool bf16, hipStream_t s);
 void launch_argmax(const ArgmaxArgs& a, int B, hipStream_t s);
 void launch_advance(const AdvanceArgs& a, int B, hipStream_t s);
