@@ -1494,13 +1494,7 @@ static int device_cus() {
 
 // one input vector and fewer row pairs than kSplitWaves: split K over the
 // waves of a block (k_gemv_splitk); false when the shape does not qualify
-#ifndef MOSHI_LPG_MAX
-#define MOSHI_LPG_MAX 8
-#endif
-#ifndef MOSHI_SPLIT_WAVES
-#define MOSHI_SPLIT_WAVES 2048
-#endif
-constexpr int kSplitWaves = MOSHI_SPLIT_WAVES;
+constexpr int kSplitWaves = 2048;
 
 template <bool BF, int SPW, int XP = XP_LOAD>
 static void splitk_launch(const GemvArgs& a, int epi, int SK, hipStream_t s) {
@@ -1567,11 +1561,15 @@ static bool gemv_splitk(const GemvArgs& a, int epi, bool bf16, hipStream_t s) {
 // loads per group and padded K of the one-vector persistent route (NB input
 // vectors), or false when x does not fit in LDS
 template <bool BF>
-static bool persist_plan(const GemvArgs& a, int NB, int* lpgo, size_t* ldso) {
+static bool persist_plan(const GemvArgs& a, int NB, int epi, int* lpgo, size_t* ldso) {
   if ((size_t)NB * a.K * sizeof(float) > 65536) return false;
   constexpr int EPL = WLoad<BF>::EPL;
   const int slots = (a.K + 64 * EPL - 1) / (64 * EPL);
-  const int lpg = std::min(slots <= 2 ? 2 : (slots <= 4 ? 4 : 8), MOSHI_LPG_MAX);
+  // QKV maps at most 4 loads per group: the 7B map has 6144 row pairs for
+  // 4096 waves, and with more, shorter units the waves that own two pairs keep
+  // their loads flowing (18.9 -> 18.3 us per layer; the evenly loaded maps are
+  // faster with 8)
+  const int lpg = std::min(slots <= 2 ? 2 : (slots <= 4 ? 4 : 8), epi == EPI_QKV ? 4 : 8);
   const int KP = ((a.K + 64 * EPL * lpg - 1) / (64 * EPL * lpg)) * 64 * EPL * lpg;
   const size_t lds_p = (size_t)NB * KP * sizeof(float);
   if (lds_p > 65536) return false;
@@ -1587,7 +1585,7 @@ static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s)
   }
   int lpg;
   size_t lds_p;
-  if (persist_plan<BF>(a, NB, &lpg, &lds_p)) {
+  if (persist_plan<BF>(a, NB, epi, &lpg, &lds_p)) {
     const int need = ((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
     dim3 grid(std::min(need, 2 * device_cus()));
     const int T = 64 * kStreamWaves;
@@ -2076,7 +2074,7 @@ bool launch_attn_wo(const AttnArgs& at, int B, int H, int hd, bool kv_bf16, Gemv
   wo.merge_ns = NS;
   wo.hd = hd;
   const bool sk = splitk_plan(wo, bf16, &SK, &spw);
-  const bool ps = bf16 ? persist_plan<true>(wo, 1, &lpg, &lds) : persist_plan<false>(wo, 1, &lpg, &lds);
+  const bool ps = bf16 ? persist_plan<true>(wo, 1, EPI_RESID, &lpg, &lds) : persist_plan<false>(wo, 1, EPI_RESID, &lpg, &lds);
   if (!sk && !ps) return false;
   launch_attn_range(at, B, H, hd, kv_bf16, NS, false, s);
   if (sk) return gemv_splitk_xp<XP_MERGE>(wo, EPI_RESID, bf16, s);
