@@ -434,43 +434,51 @@ __device__ __forceinline__ void pair_store(const GemvArgs& a, float* y, int row,
 constexpr int XP_LOAD = 0, XP_ATTN = 1, XP_MERGE = 2;
 constexpr int kMergeMaxSplits = 8;
 
-// Causal attention of head h of one query over the keys 0..P-1 (P <= NK) of a
-// flat fp32 cache; lane = head dimension (hd <= 64), lanes past hd return 0.
-// q, K and V are requested together, so the wave waits on memory once;
-// softmax with max subtraction.
-template <int NK>
-__device__ __forceinline__ float depth_attn_lane(const float* q, const KvView& kv, int b, int layer, int h, int P,
-                                                 float scale, int lane) {
+// Causal attention of NH heads h0, h0 + hs, ... of one query over the keys
+// 0..P-1 (P <= NK) of a flat fp32 cache; lane = head dimension (hd <= 64),
+// lanes past hd give 0; heads past H are not computed (their out is 0). q, K
+// and V of all NH heads are requested together, so the wave waits on memory
+// once; softmax with max subtraction.
+template <int NK, int NH>
+__device__ __forceinline__ void depth_attn_heads(const float* q, const KvView& kv, int b, int layer, int h0, int hs,
+                                                 int H, int P, float scale, int lane, float (&out)[NH]) {
   const int hd = kv.hd;
   const bool on = lane < hd;
   const int dim = on ? lane : 0;
   const float* kvb = (const float*)kv.base;
-  const long long kb = kv.offset(b, layer, 0, h, 0) + dim;
-  const long long vb = kv.offset(b, layer, 1, h, 0) + dim;
-  const float qv = q[h * hd + dim] * scale;
-  float kk[NK], vv[NK];
+  float qv[NH], kk[NH][NK], vv[NH][NK];
 #pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    const int tt = min(t, P - 1);
-    kk[t] = kvb[kb + (long long)tt * hd];
-    vv[t] = kvb[vb + (long long)tt * hd];
-  }
-  float sc[NK], m = -INFINITY;
+  for (int n = 0; n < NH; ++n) {
+    const int h = min(h0 + n * hs, H - 1);
+    const long long kb = kv.offset(b, layer, 0, h, 0) + dim;
+    const long long vb = kv.offset(b, layer, 1, h, 0) + dim;
+    qv[n] = q[h * hd + dim] * scale;
 #pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    sc[t] = wave_sum(on ? qv * kk[t] : 0.f);
-    if (t < P) m = fmaxf(m, sc[t]);
-  }
-  float l = 0.f, o = 0.f;
-#pragma unroll
-  for (int t = 0; t < NK; ++t) {
-    if (t < P) {
-      const float pr = expf(sc[t] - m);
-      l += pr;
-      o = fmaf(pr, vv[t], o);
+    for (int t = 0; t < NK; ++t) {
+      const int tt = min(t, P - 1);
+      kk[n][t] = kvb[kb + (long long)tt * hd];
+      vv[n][t] = kvb[vb + (long long)tt * hd];
     }
   }
-  return on ? o / l : 0.f;
+#pragma unroll
+  for (int n = 0; n < NH; ++n) {
+    float sc[NK], m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      sc[t] = wave_sum(on ? qv[n] * kk[n][t] : 0.f);
+      if (t < P) m = fmaxf(m, sc[t]);
+    }
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      if (t < P) {
+        const float pr = expf(sc[t] - m);
+        l += pr;
+        o = fmaf(pr, vv[n][t], o);
+      }
+    }
+    out[n] = on && h0 + n * hs < H ? o / l : 0.f;
+  }
 }
 
 // x[k .. k+3] of the temporal attention output (k a multiple of 4, so the
@@ -774,12 +782,19 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_splitk(GemvArgs a, i
   if constexpr (XP == XP_ATTN) {
     // x = the depth attention output: wave w takes heads w, w + 8, ...
     for (int k = K + tid * 4; k < KPAD; k += 64 * kStreamWaves * 4) xs4[k >> 2] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // (two heads at a time, their loads in flight together)
     float* xs = (float*)xs4;
-    const int P = a.pos_const + 1;
-    for (int h = wave; h * a.hd < K; h += kStreamWaves) {
-      const float o = P <= 8 ? depth_attn_lane<8>(a.attn_q, a.kv, 0, a.layer, h, P, a.attn_scale, lane)
-                             : depth_attn_lane<16>(a.attn_q, a.kv, 0, a.layer, h, P, a.attn_scale, lane);
-      if (lane < a.hd) xs[h * a.hd + lane] = o;
+    const int P = a.pos_const + 1, H = K / a.hd;
+    for (int h = wave; h < H; h += 2 * kStreamWaves) {
+      float o[2];
+      if (P <= 8)
+        depth_attn_heads<8, 2>(a.attn_q, a.kv, 0, a.layer, h, kStreamWaves, H, P, a.attn_scale, lane, o);
+      else
+        depth_attn_heads<16, 2>(a.attn_q, a.kv, 0, a.layer, h, kStreamWaves, H, P, a.attn_scale, lane, o);
+      if (lane < a.hd) {
+        xs[h * a.hd + lane] = o[0];
+        if (h + kStreamWaves < H) xs[(h + kStreamWaves) * a.hd + lane] = o[1];
+      }
     }
   }
   for (int k = tid * 4; XP != XP_ATTN && k < KPAD; k += 64 * kStreamWaves * 4) {
@@ -1982,8 +1997,9 @@ template <int NK>
 __global__ __launch_bounds__(64) void k_attn_depth(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int P = (a.pos ? a.pos[b] : a.pos_const) + 1;
-  const float o = depth_attn_lane<NK>(a.q + (long long)b * a.ldq, a.kv, b, a.layer, h, P, a.scale, lane);
-  if (lane < a.kv.hd) a.out[(long long)b * a.ldo + h * a.kv.hd + lane] = o;
+  float o[1];
+  depth_attn_heads<NK, 1>(a.q + (long long)b * a.ldq, a.kv, b, a.layer, h, 0, gridDim.x, P, a.scale, lane, o);
+  if (lane < a.kv.hd) a.out[(long long)b * a.ldo + h * a.kv.hd + lane] = o[0];
 }
 
 static bool depth_attn_ok(const AttnArgs& a, int hd, bool kv_bf16) {
