@@ -542,7 +542,10 @@ __global__ __launch_bounds__(64 * kStreamWaves) void k_gemv_persist(GemvArgs a) 
   const int KP = ng * GROUP;
   const int npairs = (N + 1) / 2;
   const int nw = gridDim.x * kStreamWaves;
-  const int gw = blockIdx.x * kStreamWaves + wave;
+  // row pairs go round-robin over the waves in wave-major order (wave w of
+  // every block before wave w + 1 of any), so all blocks, and so all CUs, own
+  // the same number of pairs to within one
+  const int gw = wave * gridDim.x + blockIdx.x;
   const int mine = gw < npairs ? (npairs - 1 - gw) / nw + 1 : 0;
   const int units = mine * ng;
   const char* Wb = (const char*)a.W;
@@ -1602,7 +1605,9 @@ static void gemv_dispatch_epi(const GemvArgs& a, int epi, int KC, hipStream_t s)
   size_t lds_p;
   if (persist_plan<BF>(a, NB, epi, &lpg, &lds_p)) {
     const int need = ((a.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
-    dim3 grid(std::min(need, 2 * device_cus()));
+    // two blocks per CU whenever one per CU would not hold every row pair (the
+    // wave-major assignment spreads the pairs over all of them)
+    dim3 grid(need > device_cus() ? 2 * device_cus() : need);
     const int T = 64 * kStreamWaves;
 #define MOSHI_GP(E, L) k_gemv_persist<NB, BF, E, L><<<grid, T, lds_p, s>>>(a)
 #define MOSHI_GPL(E) (lpg == 2 ? MOSHI_GP(E, 2) : (lpg == 4 ? MOSHI_GP(E, 4) : MOSHI_GP(E, 8)))
@@ -2095,7 +2100,7 @@ bool launch_attn_wo(const AttnArgs& at, int B, int H, int hd, bool kv_bf16, Gemv
   launch_attn_range(at, B, H, hd, kv_bf16, NS, false, s);
   if (sk) return gemv_splitk_xp<XP_MERGE>(wo, EPI_RESID, bf16, s);
   const int need = ((wo.N + 1) / 2 + kStreamWaves - 1) / kStreamWaves;
-  dim3 grid(std::min(need, 2 * device_cus()));
+  dim3 grid(need > device_cus() ? 2 * device_cus() : need);
   const int T = 64 * kStreamWaves;
 #define MOSHI_GM(BFV, L) k_gemv_persist<1, BFV, EPI_RESID, L, XP_MERGE><<<grid, T, lds, s>>>(wo)
   if (bf16) {
